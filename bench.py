@@ -1,0 +1,199 @@
+"""Throughput of the batch-invariant W8A16 decode projection on one MI355X.
+
+One step = one call of w8_linear_invariant on the 6144x5120 projection
+(int8 G32 weights, fp16 scales, bf16 activations) at the fixed width
+T_pad = 32 with t = 32 real columns -- the whole hot path for this workload.
+The weights rotate over enough device copies (>= 1 GiB) that the 256 MB
+Infinity Cache cannot serve them, steps are replayed from HIP graphs, and the
+time of the timed steps is taken with HIP events on the stream they run on.
+The same is measured at t = 1.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weight GB/s and TFLOP/s at t=1 and t=T_pad (% roofline); t-invariance pass"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3300)
+    p.add_argument("--warmup", type=int, default=330)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--profile-copy", action="store_true",
+                   help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the projection shards by output rows "
+              "with no reduction across GPUs, so per-GPU throughput is the one-GPU number.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import invariant_quantized_decode_amd as w8
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = synth.LINEAR_6144
+    N, K, T_pad = case.N, case.K, case.T_pad
+    d = synth.linear_6144_permuted()
+    q, s, pool = d["q"], d["s"], d["pool"]
+    wbytes = case.weight_bytes
+
+    W0 = torch.from_numpy(q).to(dev)
+    S0 = torch.from_numpy(s.view(np.int16)).to(dev)
+    copies = max(1, math.ceil((1 << 30) / wbytes))
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    Ss = [S0] + [S0.clone() for _ in range(copies - 1)]
+    X = torch.from_numpy(pool.view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((T_pad, N), dtype=torch.bfloat16, device=dev)
+
+    # ---- t-invariance on this workload: every pool column keeps its bits for t = 1..32
+    base = w8.w8_linear_invariant(W0, S0, X, T_pad, T_pad).clone()
+    inv_ok = True
+    for t in range(1, T_pad + 1):
+        cols = torch.from_numpy(d["perms"][t]).to(dev)
+        y = w8.w8_linear_invariant(W0, S0, X[cols].contiguous(), t, T_pad)
+        inv_ok &= bool(torch.equal(y.view(torch.int16), base[cols].view(torch.int16)))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream(device=dev)
+
+    def capture(t: int, count: int, start: int):
+        g = torch.cuda.CUDAGraph()
+        Xt = X[:t]
+        with torch.cuda.stream(stream):
+            w8.w8_linear_invariant(Ws[0], Ss[0], Xt, t, T_pad, y=Y)  # warm the launch path
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(count):
+                    c = (start + i) % copies
+                    w8.w8_linear_invariant(Ws[c], Ss[c], Xt, t, T_pad, y=Y)
+        return g
+
+    def measure(t: int, steps: int, warmup: int):
+        R = copies
+        g_full = capture(t, R, 0)
+        rem = steps % R
+        g_rem = capture(t, rem, 0) if rem else None
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, math.ceil(warmup / R))):
+                g_full.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            wall0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(steps // R):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - wall0
+        ms = e0.elapsed_time(e1)
+        sec_per_step = ms / 1e3 / steps
+        alg_bytes = wbytes + 2 * t * K + 2 * t * N
+        return dict(
+            t=t,
+            ms_per_step=ms / steps,
+            weight_gbs=wbytes / sec_per_step / 1e9,
+            alg_gbs=alg_bytes / sec_per_step / 1e9,
+            tflops_useful=2.0 * N * K * t / sec_per_step / 1e12,
+            tflops_executed=2.0 * N * K * T_pad / sec_per_step / 1e12,
+            wall_s=wall,
+            alg_bytes=alg_bytes,
+        )
+
+    full = measure(T_pad, args.steps, args.warmup)
+    one = measure(1, args.steps, args.warmup)
+
+    if args.profile_copy:  # a plain copy of known size, for scaling HBM byte counters
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        from invariant_quantized_decode_amd import kernel_source_digest
+        rec = json.load(open(tpath))
+        if rec.get("kernel_digest") == kernel_source_digest() and rec.get("workload") == case.name:
+            traffic = rec.get("bytes_per_launch")
+
+    roof = dict(bound="hbm", achieved=round(full["alg_gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(full["alg_gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                kernel="gemm_w8g32_fixed_width<1>", bytes_per_launch=full["alg_bytes"],
+                avg_launch_us=round(full["ms_per_step"] * 1e3, 3))
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.w8_linear(q, s, pool)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cpu = dict(value=round(reps * wbytes / el / 1e9, 4), unit="GB/s", cores=oracle.max_threads(),
+                   kind="oracle",
+                   sample=f"fp64 oracle on the full {N}x{K} projection at t={T_pad}, {reps} repetitions "
+                          f"in {el:.1f} s")
+
+    def r(v, n=3):
+        return round(v, n)
+
+    line = {
+        "metric": METRIC,
+        "value": r(full["weight_gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r(full["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "N": N, "K": K, "T_pad": T_pad, "t": T_pad,
+                   "weight_bytes": wbytes, "rotating_weight_copies": copies, "launch": "hipGraph replay"},
+        "hbm_frac_t_pad": r(full["weight_gbs"] / HBM_PEAK_GBS, 4),
+        "tflops_t_pad": {"useful": r(full["tflops_useful"]), "executed": r(full["tflops_executed"]),
+                         "mfma_frac_executed": r(full["tflops_executed"] / BF16_PEAK_TFLOPS, 4)},
+        "t1": {"value": r(one["weight_gbs"], 1), "unit": "GB/s", "ms_per_step": r(one["ms_per_step"], 5),
+               "hbm_frac": r(one["weight_gbs"] / HBM_PEAK_GBS, 4), "tflops_useful": r(one["tflops_useful"]),
+               "tflops_executed": r(one["tflops_executed"])},
+        "t_invariance": inv_ok,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

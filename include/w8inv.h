@@ -1,0 +1,172 @@
+/*
+ * w8inv.h -- C ABI of the batch-invariant W8A16 decode projection library
+ * (libw8inv.so, hand-written HIP for gfx950 / MI355X).
+ *
+ * Conventions for every entry point below
+ *  - All data pointers are DEVICE memory owned by the caller (for example
+ *    the storage of torch tensors).  The library never allocates, frees or
+ *    keeps a pointer after the call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream).  Nothing synchronises: the return value is the result of
+ *    host-side argument validation and of the launch itself, not of the
+ *    kernels' execution.
+ *  - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
+ *  - A call with t == 0 (or n == 0) validates nothing else, launches nothing
+ *    and returns W8I_OK.
+ *  - Invalid arguments return a negative w8i_status and launch nothing.  No
+ *    input is ever silently replaced by another computation.
+ *  - The library has no global state and no runtime switches: for given
+ *    arguments the arithmetic, and therefore every output bit, is fixed.
+ */
+#ifndef W8INV_H
+#define W8INV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8I_OK = 0,
+    W8I_ENULL = -1,      /* a required pointer is NULL                               */
+    W8I_ESHAPE = -2,     /* a size or leading dimension is out of range              */
+    W8I_EALIGN = -3,     /* a pointer or leading dimension breaks an alignment rule  */
+    W8I_ET = -4,         /* t < 0, t > T_pad, or T_pad not supported                 */
+    W8I_EBLOCK = -5,     /* vocabulary block width not a power of two in [256,32768] */
+    W8I_EWORKSPACE = -6, /* workspace NULL or smaller than the size query returns    */
+    W8I_EHIP = -7        /* the HIP runtime reported an error when launching         */
+} w8i_status;
+
+/* Human-readable name of a status code (static storage). */
+const char *w8i_status_string(int status);
+
+/* Library version string (static storage). */
+const char *w8i_version(void);
+
+/* ---------------------------------------------------------------------------
+ * W8A16 linear at a fixed decode width.
+ *
+ * Source: the ninfer issue on t-dependent kernel dispatch (GitHub issue 80),
+ * table "Where t selects arithmetic" row "ops::linear W8G32" (int8 weights,
+ * one scale per 32 consecutive K elements, 16-bit activations) and the
+ * "Proposal: opt-in fixed decode width" section: every call runs one kernel
+ * schedule at the padded width T_pad, padded columns are never read from the
+ * caller and never stored, columns never mix, so column j's bits do not
+ * depend on t, on j's neighbours or on the order of the columns.
+ *
+ *   y[j, n] = bf16_rne( sum_k  q[n, k] * s[n, k / 32] * x[j, k] )   j < t, n < N
+ *
+ *   W_q    int8  [N, K] row-major, codes in [-127, 127] (-128 is accepted);
+ *          16-byte aligned.
+ *   scales fp16  [N, K/32] row-major (one scale per row and 32 consecutive k);
+ *          2-byte aligned.  Subnormal and zero scales are used exactly.
+ *   x      bf16  [t, ldx] row-major: token j's K features are contiguous;
+ *          16-byte aligned, ldx >= K, ldx % 8 == 0.
+ *   y      bf16  [t, ldy] row-major: token j's N outputs are contiguous;
+ *          2-byte aligned, ldy >= N.  Only y[j, n] with j < t, n < N is written.
+ *   t      real columns, 0 <= t <= T_pad.
+ *   T_pad  fixed decode width: 16, 32, 48 or 64.  The kernel computes all
+ *          T_pad columns (the first ones real, the rest zero) for every t.
+ *   N      output rows, N >= 1 (any N: the last row strip is masked).
+ *   K      reduction length, K >= 32 and K % 32 == 0.
+ *
+ * Arithmetic, fixed for every (t, T_pad, N, device):
+ *   - int8 codes become bf16 exactly; each 32-element group's products are
+ *     summed by bf16 matrix-core instructions into fp32 starting from zero;
+ *   - that group sum is multiplied by its fp16 scale and accumulated in fp64;
+ *   - K is cut into 8 contiguous slices of whole groups, slice i covering
+ *     groups [floor(G*i/8), floor(G*(i+1)/8)), G = K/32; each slice is summed
+ *     in ascending group order and the 8 slice sums are combined by the fixed
+ *     tree ((0+1)+(2+3))+((4+5)+(6+7)).  The plan depends on K only;
+ *   - the fp64 result is rounded once to bf16, nearest-even.
+ *   No atomics, no autotuning, no choice made from t.
+ *
+ * workspace: this kernel needs none; the size query returns 0 and workspace
+ * may be NULL.
+ * ------------------------------------------------------------------------- */
+size_t w8_linear_invariant_workspace_bytes(int64_t N, int64_t K, int32_t T_pad);
+
+int w8_linear_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_t *x,
+                        int32_t t, int32_t T_pad, uint16_t *y,
+                        int64_t N, int64_t K, int64_t ldx, int64_t ldy,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Target-token logprob by fixed-width vocabulary blocks (LM-head epilogue).
+ *
+ * Source: the tokenspeed "Numerics envelopes" page, alignment.trainer table
+ * row "--logprob-order blockwise" (row max, shift, target gather, sum_exp over
+ * fixed-width vocabulary blocks with each block's own fixed tree, an fp32 left
+ * fold across blocks, negative cross-entropy), its "Logprobs" section (bf16
+ * logits are widened exactly to fp32 inside the kernel; the negated form
+ * gives -0.0 for a certain token) and the block_sumexp leaf contract
+ * paragraph (partials in vocabulary order, folded left to right).
+ *
+ * For each column j < t, with l_v = fp32(logits[j, v]):
+ *   m    = max_{v < V} l_v
+ *   e_v  = EXP32(l_v - m) for v < V (the subtraction is one fp32 operation),
+ *          +0 for the virtual padding V <= v < nb*block, nb = ceil(V/block)
+ *   P_b  = balanced pairwise fp32 tree over e_{b*block .. b*block+block-1}
+ *          in index order: T(i,1) = e_i, T(i,2w) = T(i,w) + T(i+w,w)
+ *   S    = ((P_0 + P_1) + P_2) + ... + P_{nb-1}        (fp32)
+ *   out  = -(LOG32(S) - (l_target - m))                (fp32)
+ * EXP32 / LOG32 are the correctly rounded fp32 values of e^x and ln x.
+ * A NaN logit in the row, or a target outside [0, V), gives out = NaN; a +inf
+ * logit gives NaN through the arithmetic (inf - inf).
+ *
+ *   logits  bf16 [t, ldl] row-major (column j's V logits contiguous);
+ *           2-byte aligned, ldl >= V.  (16-byte alignment with ldl % 8 == 0
+ *           selects 128-bit loads; the results are identical either way.)
+ *   targets int64 [t] token ids.
+ *   block   power of two in [256, 32768].
+ *   out     fp32 [t].
+ *   workspace device buffer of at least vocab_block_logprob_workspace_bytes()
+ *           bytes, 16-byte aligned; contents are scratch.
+ * ------------------------------------------------------------------------- */
+size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block);
+
+int vocab_block_logprob(const uint16_t *logits, const int64_t *targets, int32_t block,
+                        float *out, int32_t t, int64_t V, int64_t ldl,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Column-local glue between the projections of one decode layer.  The ninfer
+ * issue's "Where t selects arithmetic" notes that norms and other per-lane
+ * ops are invariant; these kernels keep every column's arithmetic independent
+ * of the other columns.  bf16 in and out, fp32 arithmetic, bf16 rounding
+ * nearest-even.  Pointers 2-byte aligned.
+ *
+ * w8i_rmsnorm: y[j,:] = x[j,:] * w / sqrt(mean(x[j,:]^2) + eps), w = weight
+ *   (bf16 [H]) or 1 when weight is NULL.  The sum of squares is a balanced
+ *   pairwise fp32 tree over the H features zero-padded to a power of two;
+ *   then mean = sum / H, d = sqrt(mean + eps), y = (x / d) * w, each one
+ *   correctly rounded fp32 operation.  1 <= H <= 65536.
+ * w8i_swiglu: y[j,h] = silu(g) * u with g = gate_up[j,h], u = gate_up[j,F+h]:
+ *   silu(g) = g / (1 + EXP32(-g)), fp32.
+ * w8i_residual_add: y[j,h] = a[j,h] + b[j,h] in fp32, rounded to bf16
+ *   (y may alias a or b).
+ * ------------------------------------------------------------------------- */
+int w8i_rmsnorm(const uint16_t *x, const uint16_t *weight, float eps, uint16_t *y,
+                int32_t t, int64_t H, int64_t ldx, int64_t ldy, void *stream);
+
+int w8i_swiglu(const uint16_t *gate_up, uint16_t *y, int32_t t, int64_t F,
+               int64_t ldg, int64_t ldy, void *stream);
+
+int w8i_residual_add(const uint16_t *a, const uint16_t *b, uint16_t *y, int32_t t,
+                     int64_t H, int64_t lda, int64_t ldb, int64_t ldy, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Verification hooks: the device EXP32 / LOG32 used above, applied
+ * elementwise (y[i] = EXP32(x[i]) or LOG32(x[i]), fp32, 4-byte aligned), so
+ * that tests can compare them with the correctly rounded values.
+ * ------------------------------------------------------------------------- */
+int w8i_exp32(const float *x, float *y, int64_t n, void *stream);
+int w8i_log32(const float *x, float *y, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8INV_H */

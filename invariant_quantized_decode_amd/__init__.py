@@ -1,0 +1,245 @@
+"""Batch-invariant W8A16 decode projection for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI of libw8inv.so (include/w8inv.h).  Each
+function has the name of the C entry point it calls and only marshals
+arguments: torch tensors supply device memory and the current HIP stream; every
+step of the computation runs in the library's HIP kernels.  There is no other
+implementation behind these names: if the library is missing, importing this
+package raises.
+
+Storage formats: int8 weight codes; fp16 scales (torch.float16, or int16/uint16
+bit patterns); bf16 activations and logits (torch.bfloat16); int64 targets.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8inv.so")
+
+W8I_OK = 0
+STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: "W8I_ET", -5: "W8I_EBLOCK",
+          -6: "W8I_EWORKSPACE", -7: "W8I_EHIP"}
+
+EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
+           "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
+           "w8i_residual_add", "w8i_exp32", "w8i_log32")
+
+
+class W8InvError(ValueError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {status} ({_lib.w8i_status_string(status).decode()})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.w8i_status_string.argtypes, L.w8i_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.w8i_version.argtypes, L.w8i_version.restype = [], ctypes.c_char_p
+    L.w8_linear_invariant_workspace_bytes.argtypes = [I64, I64, I32]
+    L.w8_linear_invariant_workspace_bytes.restype = SZ
+    L.w8_linear_invariant.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
+    L.w8_linear_invariant.restype = ctypes.c_int
+    L.vocab_block_logprob_workspace_bytes.argtypes = [I32, I64, I32]
+    L.vocab_block_logprob_workspace_bytes.restype = SZ
+    L.vocab_block_logprob.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
+    L.vocab_block_logprob.restype = ctypes.c_int
+    L.w8i_rmsnorm.argtypes = [P, P, F32, P, I32, I64, I64, I64, P]
+    L.w8i_swiglu.argtypes = [P, P, I32, I64, I64, I64, P]
+    L.w8i_residual_add.argtypes = [P, P, P, I32, I64, I64, I64, I64, P]
+    L.w8i_exp32.argtypes = [P, P, I64, P]
+    L.w8i_log32.argtypes = [P, P, I64, P]
+    for name in ("w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != W8I_OK:
+        raise W8InvError(fn, status)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _row_major(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def _same_gpu(*named):
+    """Every tensor must live on one GPU: a host pointer must never reach a kernel."""
+    dev = None
+    for name, ten in named:
+        if ten is None:
+            continue
+        if not isinstance(ten, torch.Tensor) or ten.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if dev is None:
+            dev = ten.device
+        elif ten.device != dev:
+            raise ValueError(f"{name} is on {ten.device}, expected {dev}")
+
+
+def _dtype(ten, name, *dtypes):
+    if ten is not None and ten.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {ten.dtype}")
+
+
+def version() -> str:
+    return _lib.w8i_version().decode()
+
+
+def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, t: int, T_pad: int,
+                        y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[:t] = bf16(dequant(W_q, scales) @ x[:t]^T) at the fixed width T_pad.
+
+    W_q int8 [N, K]; scales fp16 [N, K/32]; x bf16 [>=t, K] (token rows); y bf16 [t, N] (allocated if None).
+    """
+    if W_q.dtype != torch.int8 or W_q.dim() != 2 or not W_q.is_contiguous():
+        raise ValueError("W_q must be a contiguous int8 [N, K] tensor")
+    N, K = W_q.shape
+    if scales.dtype not in (torch.float16, torch.int16) or tuple(scales.shape) != (N, K // 32) \
+            or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp16 [N, K/32] tensor")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.size(1) != K or x.size(0) < t:
+        raise ValueError("x must be a bf16 [>=t, K] tensor")
+    ldx = _row_major(x, "x")
+    if y is None:
+        y = torch.empty((t, N), dtype=torch.bfloat16, device=W_q.device)
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != N or y.size(0) < t:
+        raise ValueError("y must be a bf16 [>=t, N] tensor")
+    ldy = _row_major(y, "y")
+    _same_gpu(("W_q", W_q), ("scales", scales), ("x", x), ("y", y))
+    st = _lib.w8_linear_invariant(_ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y), N, K, ldx, ldy,
+                                  None, 0, ctypes.c_void_p(_stream(W_q.device)))
+    _check("w8_linear_invariant", st)
+    return y
+
+
+def vocab_block_logprob_workspace_bytes(t: int, V: int, block: int) -> int:
+    return int(_lib.vocab_block_logprob_workspace_bytes(int(t), int(V), int(block)))
+
+
+def vocab_block_logprob(logits: torch.Tensor, targets: torch.Tensor, block: int, out: torch.Tensor | None = None,
+                        t: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [t] target logprobs by `block`-wide vocabulary blocks.  logits bf16 [t, V] (rows contiguous)."""
+    if logits.dtype != torch.bfloat16 or logits.dim() != 2:
+        raise ValueError("logits must be a bf16 [t, V] tensor")
+    t = logits.size(0) if t is None else int(t)
+    V = logits.size(1)
+    ldl = _row_major(logits, "logits")
+    if targets.dtype != torch.int64 or targets.numel() < t or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int64 [t] tensor")
+    if out is None:
+        out = torch.empty(t, dtype=torch.float32, device=logits.device)
+    _dtype(out, "out", torch.float32)
+    if out.numel() < t or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [t] tensor")
+    need = vocab_block_logprob_workspace_bytes(t, V, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    _same_gpu(("logits", logits), ("targets", targets), ("out", out), ("workspace", workspace))
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    st = _lib.vocab_block_logprob(_ptr(logits), _ptr(targets), int(block), _ptr(out), t, V, ldl, _ptr(workspace),
+                                  workspace.numel(), ctypes.c_void_p(_stream(logits.device)))
+    _check("vocab_block_logprob", st)
+    return out
+
+
+def w8i_rmsnorm(x: torch.Tensor, eps: float, weight: torch.Tensor | None = None,
+                y: torch.Tensor | None = None) -> torch.Tensor:
+    t, H = x.shape
+    ldx = _row_major(x, "x")
+    y = torch.empty((t, H), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _same_gpu(("x", x), ("weight", weight), ("y", y))
+    _dtype(x, "x", torch.bfloat16), _dtype(weight, "weight", torch.bfloat16), _dtype(y, "y", torch.bfloat16)
+    if weight is not None and (weight.numel() < H or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous bf16 [H] tensor")
+    if y.shape[0] < t or y.shape[1] != H:
+        raise ValueError("y must be bf16 [t, H]")
+    st = _lib.w8i_rmsnorm(_ptr(x), _ptr(weight), float(eps), _ptr(y), t, H, ldx, _row_major(y, "y"),
+                          ctypes.c_void_p(_stream(x.device)))
+    _check("w8i_rmsnorm", st)
+    return y
+
+
+def w8i_swiglu(gate_up: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    t, F2 = gate_up.shape
+    F = F2 // 2
+    y = torch.empty((t, F), dtype=torch.bfloat16, device=gate_up.device) if y is None else y
+    _same_gpu(("gate_up", gate_up), ("y", y))
+    _dtype(gate_up, "gate_up", torch.bfloat16), _dtype(y, "y", torch.bfloat16)
+    if y.shape[0] < t or y.shape[1] != F:
+        raise ValueError("y must be bf16 [t, F]")
+    st = _lib.w8i_swiglu(_ptr(gate_up), _ptr(y), t, F, _row_major(gate_up, "gate_up"), _row_major(y, "y"),
+                         ctypes.c_void_p(_stream(gate_up.device)))
+    _check("w8i_swiglu", st)
+    return y
+
+
+def w8i_residual_add(a: torch.Tensor, b: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    t, H = a.shape
+    y = torch.empty((t, H), dtype=torch.bfloat16, device=a.device) if y is None else y
+    _same_gpu(("a", a), ("b", b), ("y", y))
+    for name, ten in (("a", a), ("b", b), ("y", y)):
+        _dtype(ten, name, torch.bfloat16)
+        if ten.dim() != 2 or ten.shape[0] < t or ten.shape[1] != H:
+            raise ValueError(f"{name} must be bf16 [t, H]")
+    st = _lib.w8i_residual_add(_ptr(a), _ptr(b), _ptr(y), t, H, _row_major(a, "a"), _row_major(b, "b"),
+                               _row_major(y, "y"), ctypes.c_void_p(_stream(a.device)))
+    _check("w8i_residual_add", st)
+    return y
+
+
+def w8i_exp32(x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    x = x.contiguous()
+    y = torch.empty_like(x) if y is None else y
+    _same_gpu(("x", x), ("y", y))
+    _dtype(x, "x", torch.float32), _dtype(y, "y", torch.float32)
+    if y.numel() < x.numel() or not y.is_contiguous():
+        raise ValueError("y must be a contiguous fp32 tensor as large as x")
+    _check("w8i_exp32", _lib.w8i_exp32(_ptr(x), _ptr(y), x.numel(), ctypes.c_void_p(_stream(x.device))))
+    return y
+
+
+def w8i_log32(x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    x = x.contiguous()
+    y = torch.empty_like(x) if y is None else y
+    _same_gpu(("x", x), ("y", y))
+    _dtype(x, "x", torch.float32), _dtype(y, "y", torch.float32)
+    if y.numel() < x.numel() or not y.is_contiguous():
+        raise ValueError("y must be a contiguous fp32 tensor as large as x")
+    _check("w8i_log32", _lib.w8i_log32(_ptr(x), _ptr(y), x.numel(), ctypes.c_void_p(_stream(x.device))))
+    return y
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the GEMM kernel's sources: identifies which kernel a stored counter profile measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("w8inv_gemm.hip", "w8inv_math.h", "w8inv_internal.h"):
+        with open(os.path.join(_HERE, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]

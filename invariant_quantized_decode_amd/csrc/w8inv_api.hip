@@ -1,0 +1,132 @@
+// w8inv_api.hip -- the extern "C" entry points of libw8inv.so: argument
+// validation on the host, then launches on the caller's stream.  Nothing
+// here allocates, frees or synchronises.  The rules checked are the ones
+// stated for each entry point in include/w8inv.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w8inv.h"
+#include "w8inv_internal.h"
+
+using namespace w8i;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+const char* w8i_status_string(int status) {
+    switch (status) {
+        case W8I_OK: return "W8I_OK";
+        case W8I_ENULL: return "W8I_ENULL: a required pointer is NULL";
+        case W8I_ESHAPE: return "W8I_ESHAPE: a size or leading dimension is out of range";
+        case W8I_EALIGN: return "W8I_EALIGN: a pointer or leading dimension breaks an alignment rule";
+        case W8I_ET: return "W8I_ET: t < 0, t > T_pad, or T_pad not supported";
+        case W8I_EBLOCK: return "W8I_EBLOCK: block width not a power of two in [256, 32768]";
+        case W8I_EWORKSPACE: return "W8I_EWORKSPACE: workspace NULL or too small";
+        case W8I_EHIP: return "W8I_EHIP: the HIP runtime reported an error";
+        default: return "unknown w8i status";
+    }
+}
+
+const char* w8i_version(void) { return "w8inv 0.1 (gfx950)"; }
+
+size_t w8_linear_invariant_workspace_bytes(int64_t N, int64_t K, int32_t T_pad) {
+    (void)N;
+    (void)K;
+    (void)T_pad;
+    return 0;
+}
+
+int w8_linear_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, int32_t t, int32_t T_pad,
+                        uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
+    if (t < 0 || t > T_pad) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!W_q || !scales || !x || !y) return W8I_ENULL;
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxDim * 64)
+        return W8I_ESHAPE;
+    if (ldx < K || ldy < N) return W8I_ESHAPE;
+    if (!aligned(W_q, 16) || !aligned(x, 16) || ldx % 8 != 0 || !aligned(scales, 2) || !aligned(y, 2))
+        return W8I_EALIGN;
+    if ((N + 31) / 32 > 0x7fffffffLL) return W8I_ESHAPE;
+    return launch_linear(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
+}
+
+size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) {
+    if (t <= 0 || V <= 0 || block < 256 || block > 32768 || (block & (block - 1)) != 0) return 0;
+    return logprob_workspace_bytes(t, V, block);
+}
+
+int vocab_block_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
+                        int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, void* stream) {
+    if (block < 256 || block > 32768 || (block & (block - 1)) != 0) return W8I_EBLOCK;
+    if (t < 0 || t > 65535) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!logits || !targets || !out) return W8I_ENULL;
+    if (V < 1 || V > kMaxDim || ldl < V) return W8I_ESHAPE;
+    if ((V + block - 1) / block > 0x7fffffffLL) return W8I_ESHAPE;
+    if (!aligned(logits, 2) || !aligned(targets, 8) || !aligned(out, 4)) return W8I_EALIGN;
+    if (!workspace || workspace_bytes < logprob_workspace_bytes(t, V, block)) return W8I_EWORKSPACE;
+    if (!aligned(workspace, 16)) return W8I_EALIGN;
+    return launch_logprob(logits, targets, block, out, t, V, ldl, workspace, as_stream(stream));
+}
+
+int w8i_rmsnorm(const uint16_t* x, const uint16_t* weight, float eps, uint16_t* y, int32_t t, int64_t H, int64_t ldx,
+                int64_t ldy, void* stream) {
+    if (t < 0 || t > 0x7fffffff) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!x || !y) return W8I_ENULL;
+    if (H < 1 || H > 65536 || ldx < H || ldy < H) return W8I_ESHAPE;
+    if (!aligned(x, 2) || !aligned(y, 2) || (weight && !aligned(weight, 2))) return W8I_EALIGN;
+    return launch_rmsnorm(x, weight, eps, y, t, H, ldx, ldy, as_stream(stream));
+}
+
+int w8i_swiglu(const uint16_t* gate_up, uint16_t* y, int32_t t, int64_t F, int64_t ldg, int64_t ldy, void* stream) {
+    if (t < 0 || t > 65535) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!gate_up || !y) return W8I_ENULL;
+    if (F < 1 || F > kMaxDim || ldg < 2 * F || ldy < F) return W8I_ESHAPE;
+    if (!aligned(gate_up, 2) || !aligned(y, 2)) return W8I_EALIGN;
+    return launch_swiglu(gate_up, y, t, F, ldg, ldy, as_stream(stream));
+}
+
+int w8i_residual_add(const uint16_t* a, const uint16_t* b, uint16_t* y, int32_t t, int64_t H, int64_t lda,
+                     int64_t ldb, int64_t ldy, void* stream) {
+    if (t < 0 || t > 65535) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!a || !b || !y) return W8I_ENULL;
+    if (H < 1 || H > kMaxDim || lda < H || ldb < H || ldy < H) return W8I_ESHAPE;
+    if (!aligned(a, 2) || !aligned(b, 2) || !aligned(y, 2)) return W8I_EALIGN;
+    return launch_residual_add(a, b, y, t, H, lda, ldb, ldy, as_stream(stream));
+}
+
+int w8i_exp32(const float* x, float* y, int64_t n, void* stream) {
+    if (n < 0) return W8I_ESHAPE;
+    if (n == 0) return W8I_OK;
+    if (!x || !y) return W8I_ENULL;
+    if (!aligned(x, 4) || !aligned(y, 4)) return W8I_EALIGN;
+    if (n > ((int64_t)1 << 38)) return W8I_ESHAPE;
+    return launch_exp32(x, y, n, as_stream(stream));
+}
+
+int w8i_log32(const float* x, float* y, int64_t n, void* stream) {
+    if (n < 0) return W8I_ESHAPE;
+    if (n == 0) return W8I_OK;
+    if (!x || !y) return W8I_ENULL;
+    if (!aligned(x, 4) || !aligned(y, 4)) return W8I_EALIGN;
+    if (n > ((int64_t)1 << 38)) return W8I_ESHAPE;
+    return launch_log32(x, y, n, as_stream(stream));
+}
+
+}  // extern "C"

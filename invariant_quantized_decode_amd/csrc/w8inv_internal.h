@@ -1,0 +1,37 @@
+// w8inv_internal.h -- declarations shared by the library's translation units
+// (not part of the public ABI; the public header is include/w8inv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w8inv.h"
+
+namespace w8i {
+
+constexpr int kGroup = 32;   // K elements per fp16 scale (W8G32)
+constexpr int kKSlices = 8;  // fixed number of K-slices per output, for every shape
+
+// First group of K-slice i when K holds G groups: floor(G * i / 8).  The
+// whole K-reduction plan is this function of K alone.
+__host__ __device__ __forceinline__ int64_t kslice_begin(int64_t G, int i) {
+    return (G * i) / kKSlices;
+}
+
+int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
+                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+
+size_t logprob_workspace_bytes(int t, int64_t V, int block);
+int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,
+                   int64_t ldl, void* ws, hipStream_t stream);
+
+int launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int t, int64_t H, int64_t ldx,
+                   int64_t ldy, hipStream_t stream);
+int launch_swiglu(const uint16_t* gu, uint16_t* y, int t, int64_t F, int64_t ldg, int64_t ldy,
+                  hipStream_t stream);
+int launch_residual_add(const uint16_t* a, const uint16_t* b, uint16_t* y, int t, int64_t H, int64_t lda,
+                        int64_t ldb, int64_t ldy, hipStream_t stream);
+int launch_exp32(const float* x, float* y, int64_t n, hipStream_t stream);
+int launch_log32(const float* x, float* y, int64_t n, hipStream_t stream);
+
+}  // namespace w8i

@@ -1,0 +1,257 @@
+// w8inv_logprob.hip -- target-token logprob by fixed-width vocabulary blocks.
+//
+// Method: the tokenspeed "Numerics envelopes" page, alignment.trainer table
+// row "--logprob-order blockwise", the "Logprobs" section and the
+// block_sumexp leaf contract paragraph: row max, shift by it, sum of exps per
+// fixed-width vocabulary block with each block in its own fixed tree, block
+// partials in vocabulary order folded left to right in fp32, then
+// out = -(log(sum) - (target - max)).
+//
+// Three launches on the caller's stream:
+//  1. block_max    grid (nb, t): exact max (and NaN flag) of each block.
+//  2. block_sumexp grid (nb, t): row max from the block maxima (exact), then
+//     the block partial in the canonical pairwise tree: thread i owns the E
+//     contiguous elements [i*E, (i+1)*E) and reduces them pairwise in
+//     registers, the wave combines lanes with xor-1 .. xor-32 butterflies
+//     (each step adds two adjacent subtrees; fp32 addition is commutative, so
+//     both lanes of a pair hold the same bits), and the four waves' subtrees
+//     are added as (w0 + w1) + (w2 + w3).  Every step is a node of
+//     T(i,2w) = T(i,w) + T(i+w,w) over the block.
+//  3. fold         one thread per column: S = ((P0 + P1) + P2) + ...,
+//     LOG32(S), target gather, final subtraction and negation.
+// Logits are bf16, widened exactly in registers.  Indices >= V are virtual
+// -inf logits: they contribute +0 to a block and nothing to the max.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w8inv_internal.h"
+#include "w8inv_math.h"
+
+namespace w8i {
+
+constexpr int kLpThreads = 256;
+
+template <int C, bool VEC>
+__device__ __forceinline__ void load_chunk(const uint16_t* row, int64_t v0, int64_t V, float (&x)[C],
+                                           bool (&ok)[C]) {
+    if constexpr (VEC && C == 8) {
+        if (v0 + 8 <= V) {
+            const uint4 q = *reinterpret_cast<const uint4*>(row + v0);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(w[i] << 16);
+                x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+                ok[2 * i] = ok[2 * i + 1] = true;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        ok[i] = v0 + i < V;
+        x[i] = ok[i] ? bf16_to_f32(row[v0 + i]) : 0.0f;
+    }
+}
+
+template <int E, bool VEC>
+__global__ __launch_bounds__(kLpThreads) void lp_block_max(const uint16_t* __restrict__ L, int64_t V, int64_t ldl,
+                                                           int nb, float* __restrict__ M) {
+    constexpr int C = E < 8 ? E : 8;
+    __shared__ float wmax[kLpThreads / 64];
+    __shared__ int wnan[kLpThreads / 64];
+    const int b = blockIdx.x, j = blockIdx.y;
+    const uint16_t* row = L + (int64_t)j * ldl;
+    const int64_t base = (int64_t)b * (E * kLpThreads) + (int64_t)threadIdx.x * E;
+    float m = -__builtin_inff();
+    int nan = 0;
+#pragma unroll
+    for (int ci = 0; ci < E / C; ++ci) {
+        float x[C];
+        bool ok[C];
+        load_chunk<C, VEC>(row, base + ci * C, V, x, ok);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (ok[i]) {
+                if (x[i] != x[i]) nan = 1;
+                else m = __builtin_fmaxf(m, x[i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        m = __builtin_fmaxf(m, __shfl_xor(m, off));
+        nan |= __shfl_xor(nan, off);
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        wmax[wave] = m;
+        wnan[wave] = nan;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float mm = wmax[0];
+        int nn = wnan[0];
+#pragma unroll
+        for (int w = 1; w < kLpThreads / 64; ++w) {
+            mm = __builtin_fmaxf(mm, wmax[w]);
+            nn |= wnan[w];
+        }
+        M[(int64_t)j * nb + b] = nn ? __builtin_nanf("") : mm;
+    }
+}
+
+// max over the block maxima of column j (NaN if any block saw a NaN)
+__device__ __forceinline__ float row_max_from_blocks(const float* M, int nb, int j, bool& nan) {
+    float m = -__builtin_inff();
+    nan = false;
+    for (int i = 0; i < nb; ++i) {
+        const float v = M[(int64_t)j * nb + i];
+        if (v != v) nan = true;
+        else m = __builtin_fmaxf(m, v);
+    }
+    return m;
+}
+
+template <int E, bool VEC>
+__global__ __launch_bounds__(kLpThreads) void lp_block_sumexp(const uint16_t* __restrict__ L, int64_t V,
+                                                              int64_t ldl, int nb, const float* __restrict__ M,
+                                                              float* __restrict__ P) {
+    constexpr int C = E < 8 ? E : 8;
+    constexpr int NC = E / C;
+    __shared__ float wsum[kLpThreads / 64];
+    __shared__ float s_max;
+    __shared__ int s_nan;
+    const int b = blockIdx.x, j = blockIdx.y;
+    if (threadIdx.x == 0) {
+        bool nan;
+        s_max = row_max_from_blocks(M, nb, j, nan);
+        s_nan = nan;
+    }
+    __syncthreads();
+    if (s_nan) {
+        if (threadIdx.x == 0) P[(int64_t)j * nb + b] = __builtin_nanf("");
+        return;
+    }
+    const float m = s_max;
+    const uint16_t* row = L + (int64_t)j * ldl;
+    const int64_t base = (int64_t)b * (E * kLpThreads) + (int64_t)threadIdx.x * E;
+
+    float cs[NC];
+#pragma unroll
+    for (int ci = 0; ci < NC; ++ci) {
+        float x[C];
+        bool ok[C];
+        load_chunk<C, VEC>(row, base + ci * C, V, x, ok);
+        float e[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const float shifted = x[i] - m;
+            e[i] = ok[i] ? exp32(shifted) : 0.0f;
+        }
+#pragma unroll
+        for (int w = 1; w < C; w *= 2)
+#pragma unroll
+            for (int i = 0; i < C; i += 2 * w) e[i] = e[i] + e[i + w];
+        cs[ci] = e[0];
+    }
+#pragma unroll
+    for (int w = 1; w < NC; w *= 2)
+#pragma unroll
+        for (int i = 0; i < NC; i += 2 * w) cs[i] = cs[i] + cs[i + w];
+    float s = cs[0];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) s = s + __shfl_xor(s, off);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) wsum[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) P[(int64_t)j * nb + b] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+__global__ void lp_fold(const uint16_t* __restrict__ L, int64_t V, int64_t ldl, const int64_t* __restrict__ targets,
+                        int nb, const float* __restrict__ M, const float* __restrict__ P, float* __restrict__ out,
+                        int t) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= t) return;
+    bool nan;
+    const float m = row_max_from_blocks(M, nb, j, nan);
+    float S = P[(int64_t)j * nb];
+    for (int b = 1; b < nb; ++b) S = S + P[(int64_t)j * nb + b];
+    const int64_t tg = targets[j];
+    if (nan || tg < 0 || tg >= V) {
+        out[j] = __builtin_nanf("");
+        return;
+    }
+    const float Lg = log32(S);
+    const float st = bf16_to_f32(L[(int64_t)j * ldl + tg]) - m;
+    const float d = Lg - st;
+    out[j] = -d;
+}
+
+static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+size_t logprob_workspace_bytes(int t, int64_t V, int block) {
+    const int64_t nb = (V + block - 1) / block;
+    return (size_t)(2 * round_up((int64_t)t * nb * (int64_t)sizeof(float), 256));
+}
+
+template <int E>
+static void launch_lp_e(const uint16_t* L, int64_t V, int64_t ldl, int nb, int t, float* M, float* P, bool vec,
+                        hipStream_t stream) {
+    const dim3 grid(nb, t), block(kLpThreads);
+    if constexpr (E >= 8) {
+        if (vec) {
+            hipLaunchKernelGGL((lp_block_max<E, true>), grid, block, 0, stream, L, V, ldl, nb, M);
+            hipLaunchKernelGGL((lp_block_sumexp<E, true>), grid, block, 0, stream, L, V, ldl, nb, M, P);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((lp_block_max<E, false>), grid, block, 0, stream, L, V, ldl, nb, M);
+    hipLaunchKernelGGL((lp_block_sumexp<E, false>), grid, block, 0, stream, L, V, ldl, nb, M, P);
+}
+
+int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V, int64_t ldl,
+                   void* ws, hipStream_t stream) {
+    const int64_t nb = (V + block - 1) / block;
+    float* M = static_cast<float*>(ws);
+    float* P = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        round_up((int64_t)t * nb * (int64_t)sizeof(float), 256));
+    const bool vec = (reinterpret_cast<uintptr_t>(L) % 16 == 0) && (ldl % 8 == 0);
+    switch (block / kLpThreads) {
+        case 1: launch_lp_e<1>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 2: launch_lp_e<2>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 4: launch_lp_e<4>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 8: launch_lp_e<8>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 16: launch_lp_e<16>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 32: launch_lp_e<32>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 64: launch_lp_e<64>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        case 128: launch_lp_e<128>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
+        default: return W8I_EBLOCK;
+    }
+    hipLaunchKernelGGL(lp_fold, dim3((t + 63) / 64), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out, t);
+    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+}
+
+// ------------------------------------------------------- verification hooks
+
+__global__ void exp32_kernel(const float* __restrict__ x, float* __restrict__ y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = exp32(x[i]);
+}
+
+__global__ void log32_kernel(const float* __restrict__ x, float* __restrict__ y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = log32(x[i]);
+}
+
+int launch_exp32(const float* x, float* y, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(exp32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, y, n);
+    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+}
+
+int launch_log32(const float* x, float* y, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(log32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, y, n);
+    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+}
+
+}  // namespace w8i

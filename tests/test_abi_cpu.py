@@ -1,0 +1,107 @@
+"""The C ABI on the host side (no GPU): the library loads, exports every entry point that
+include/w8inv.h declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8inv.h")
+
+w8 = pytest.importorskip("invariant_quantized_decode_amd")
+L = w8.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8[a-z0-9_]*|vocab_[a-z0-9_]*)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(w8.EXPORTS)
+
+
+def test_status_strings_and_version():
+    assert L.w8i_status_string(0) == b"W8I_OK"
+    for code in range(-7, 0):
+        assert L.w8i_status_string(code).decode().startswith(w8.STATUS[code])
+    assert b"gfx950" in L.w8i_version()
+
+
+def fake(addr):
+    """A non-NULL pointer value the validation layer can inspect; never dereferenced on failure paths."""
+    return ctypes.c_void_p(addr)
+
+
+A = 0x10000  # 16-byte aligned dummy address
+
+
+def linear(W=A, S=A, X=A, t=4, T=32, Y=A, N=64, K=256, ldx=256, ldy=64):
+    return L.w8_linear_invariant(fake(W) if W else None, fake(S) if S else None, fake(X) if X else None, t, T,
+                                 fake(Y) if Y else None, N, K, ldx, ldy, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=24), -4), (dict(T=128), -4), (dict(t=33), -4), (dict(t=-1), -4),
+    (dict(W=0), -1), (dict(Y=0), -1), (dict(X=0), -1), (dict(S=0), -1),
+    (dict(K=100, ldx=100), -2), (dict(K=0, ldx=0), -2), (dict(N=0), -2), (dict(ldx=128), -2), (dict(ldy=32), -2),
+    (dict(W=A + 8), -3), (dict(X=A + 4), -3), (dict(ldx=260), -3), (dict(S=A + 1), -3), (dict(Y=A + 1), -3),
+])
+def test_linear_rejects_invalid_arguments(kw, code):
+    assert linear(**kw) == code
+
+
+def test_linear_t_zero_is_a_no_op():
+    assert linear(t=0, W=0, S=0, X=0, Y=0) == 0
+    assert L.w8_linear_invariant_workspace_bytes(6144, 5120, 32) == 0
+
+
+def logprob(Lg=A, T=A, block=4096, out=A, t=4, V=248320, ldl=248320, ws=A, wsb=1 << 20):
+    return L.vocab_block_logprob(fake(Lg) if Lg else None, fake(T) if T else None, block, fake(out) if out else None,
+                                 t, V, ldl, fake(ws) if ws else None, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=1000), -5), (dict(block=128), -5), (dict(block=65536), -5),
+    (dict(t=-1), -4), (dict(Lg=0), -1), (dict(T=0), -1), (dict(out=0), -1),
+    (dict(V=0, ldl=0), -2), (dict(ldl=1000), -2),
+    (dict(Lg=A + 1), -3), (dict(T=A + 4), -3), (dict(out=A + 2), -3),
+    (dict(ws=0), -6), (dict(wsb=100), -6), (dict(ws=A + 4), -3),
+])
+def test_logprob_rejects_invalid_arguments(kw, code):
+    assert logprob(**kw) == code
+
+
+def test_logprob_workspace_size():
+    nb = (248320 + 4095) // 4096
+    need = L.vocab_block_logprob_workspace_bytes(32, 248320, 4096)
+    assert need >= 2 * 32 * nb * 4 and need % 256 == 0
+    assert L.vocab_block_logprob_workspace_bytes(32, 248320, 1000) == 0
+    assert logprob(t=0, Lg=0, T=0, out=0, ws=0) == 0
+
+
+def test_glue_and_hooks_reject_invalid_arguments():
+    assert L.w8i_rmsnorm(None, None, ctypes.c_float(1e-6), fake(A), 2, 64, 64, 64, None) == -1
+    assert L.w8i_rmsnorm(fake(A), None, ctypes.c_float(1e-6), fake(A), 2, 70000, 70000, 70000, None) == -2
+    assert L.w8i_swiglu(fake(A), fake(A), 2, 64, 100, 64, None) == -2
+    assert L.w8i_residual_add(fake(A), fake(A + 1), fake(A), 2, 64, 64, 64, 64, None) == -3
+    assert L.w8i_exp32(fake(A), fake(A + 2), 10, None) == -3
+    assert L.w8i_log32(None, fake(A), 10, None) == -1
+    assert L.w8i_exp32(None, None, 0, None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((64, 256), dtype=torch.int8)
+    s = torch.zeros((64, 8), dtype=torch.float16)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w8.w8_linear_invariant(q, s, x, 4, 32, y=torch.zeros((4, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        w8.w8i_exp32(torch.zeros(8), y=torch.zeros(8))

@@ -1,0 +1,168 @@
+"""Block logprob and the EXP32 / LOG32 device functions on the GPU, through the C ABI.
+
+The fp32 arithmetic is fixed step by step (tokenspeed "Numerics envelopes",
+alignment.trainer "--logprob-order blockwise"; "Logprobs" section; block_sumexp
+leaf contract), and EXP32/LOG32 are correctly rounded, so the GPU is expected to
+equal the fixed-order fp32 oracle bit for bit; the pass bar is 1e-5 absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import ln_rn32
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import invariant_quantized_decode_amd as w8  # noqa: E402
+from tests.gpu_util import DEV, bf16, bits, f16, f32, host, i8, say  # noqa: E402
+
+
+def f32bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def gpu_logprob(logits_bits, targets, block, pad_to=None):
+    Ld = bf16(logits_bits)
+    if pad_to is not None:  # a strided (ldl > V) view, unaligned rows
+        t, V = logits_bits.shape
+        buf = torch.zeros((t, pad_to), dtype=torch.bfloat16, device=DEV)
+        buf[:, :V] = Ld
+        Ld = buf[:, :V]
+    return host(w8.vocab_block_logprob(Ld, torch.from_numpy(np.asarray(targets, np.int64)).to(DEV), block))
+
+
+def compare(out, want, label):
+    diff = np.abs(out.astype(np.float64) - want.astype(np.float64))
+    both_nan = np.isnan(out) & np.isnan(want)
+    diff[both_nan] = 0
+    nbits = int(np.sum(f32bits(out) != f32bits(want)) - np.sum(both_nan & (f32bits(out) != f32bits(want))))
+    say(f"{label}: max |diff| {float(np.nanmax(diff)) if diff.size else 0:.3g}, {nbits} not bitwise equal")
+    assert not np.any(np.isnan(diff)) and np.all(diff <= 1e-5), label
+    return nbits
+
+
+@pytest.mark.parametrize("V,block,std,t", [
+    (785, 256, 3.0, 9), (5000, 1024, 8.0, 7), (248320, 4096, 105.0, 32), (100000, 32768, 20.0, 3),
+    (4096, 4096, 1.0, 5), (70000, 2048, 0.5, 4), (248320, 512, 105.0, 2)])
+def test_random_logits_match_fixed_order_oracle(V, block, std, t):
+    say(f"case logprob V={V} block={block} std={std}")
+    logits, targets = synth.random_logits(V + block, t, V, std=std)
+    out = gpu_logprob(logits, targets, block)
+    want = oracle.block_logprob(logits, targets, block)
+    assert compare(out, want, f"V={V} block={block}") == 0
+
+
+def test_unaligned_rows_give_identical_bits():
+    logits, targets = synth.random_logits(3, 6, 9000, std=4.0)
+    say("case logprob strided rows")
+    a = gpu_logprob(logits, targets, 4096)
+    b = gpu_logprob(logits, targets, 4096, pad_to=9003)
+    assert np.array_equal(f32bits(a), f32bits(b))
+
+
+def test_closed_forms():
+    V = 248320
+    say("case logprob closed forms")
+    uni = np.full((2, V), 0x4040, dtype=np.uint16)  # 3.0
+    out = gpu_logprob(uni, [0, V - 1], 4096)
+    assert np.all(out == -ln_rn32(V))
+    row = np.full(V, synth.f32_to_bf16_bits(np.array([-150.0], np.float32))[0], dtype=np.uint16)
+    row[4321] = synth.f32_to_bf16_bits(np.array([2.5], np.float32))[0]
+    out = gpu_logprob(np.stack([row, row]), [4321, 17], 4096)
+    assert out[0] == 0 and math.copysign(1.0, out[0]) < 0 and out[1] == np.float32(-152.5)
+    k = 7
+    tie = np.full(V, synth.f32_to_bf16_bits(np.array([-120.0], np.float32))[0], dtype=np.uint16)
+    idx = np.random.default_rng(0).choice(V, size=k, replace=False)
+    tie[idx] = 0x3F80
+    out = gpu_logprob(tie[None], [idx[0]], 4096)
+    assert out[0] == -ln_rn32(k)
+
+
+def test_nan_inf_and_bad_targets():
+    logits, _ = synth.random_logits(2, 5, 3000, std=2.0)
+    logits[0, 13] = 0x7FC0
+    logits[1, 7] = 0x7F80
+    say("case logprob NaN/inf/targets")
+    out = gpu_logprob(logits, [0, 0, -1, 3000, 3], 1024)
+    assert np.all(np.isnan(out[:4])) and np.isfinite(out[4])
+
+
+# ---------------------------------------------------------------- EXP32 / LOG32
+def test_exp32_matches_correctly_rounded_oracle_on_samples():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.uniform(-104, 89, 2_000_000), rng.uniform(-110, -85, 500_000),
+                        rng.uniform(-1e-3, 1e-3, 100_000), rng.uniform(88.5, 89.5, 10_000)]).astype(np.float32)
+    x = np.concatenate([x, np.array([0, -0.0, np.nan, np.inf, -np.inf, 1e-45, -1e-45, 88.72283, -103.97208],
+                                    np.float32)])
+    say("case exp32 samples")
+    got = host(w8.w8i_exp32(f32(x)))
+    want = oracle.exp32(x)
+    same = (f32bits(got) == f32bits(want)) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), f"{int((~same).sum())} mismatches, e.g. x={x[~same][:5]}"
+
+
+def test_log32_matches_correctly_rounded_oracle_on_samples():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.uniform(1, 2, 500_000), np.exp2(rng.uniform(-149, 128, 1_000_000)),
+                        1 + np.arange(1, 20000) * 2.0 ** -23]).astype(np.float32)
+    x = np.concatenate([x, np.array([1.0, 0.0, -1.0, np.inf, np.nan, 248320.0, 1e-45], np.float32)])
+    say("case log32 samples")
+    got = host(w8.w8i_log32(f32(x)))
+    want = oracle.log32(x)
+    same = (f32bits(got) == f32bits(want)) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), f"{int((~same).sum())} mismatches, e.g. x={x[~same][:5]}"
+
+
+@pytest.mark.slow
+def test_exp32_exhaustive_over_the_used_range():
+    """Every binary32 x in [-104, 89]: the device EXP32 equals the correctly rounded value."""
+    ranges = [(0x80000000, 0xC2D00000 - 0x80000000 + 1), (0x00000000, 0x42B20000 + 1)]  # [-104,-0], [0,89]
+    chunk = 1 << 26
+    total = bad = 0
+    for start, count in ranges:
+        for off in range(0, count, chunk):
+            n = min(chunk, count - off)
+            xb = (np.arange(n, dtype=np.uint64) + start + off).astype(np.uint32)
+            x = xb.view(np.float32)
+            got = host(w8.w8i_exp32(f32(x)))
+            want = oracle.exp32_bits(start + off, n)
+            bad += int(np.sum(f32bits(got) != f32bits(want)))
+            total += n
+    say(f"exp32 exhaustive: {total} inputs, {bad} mismatches")
+    assert bad == 0
+
+
+# ---------------------------------------------------------------- head workload
+@pytest.mark.slow
+def test_vocab_head_and_logprob_workload():
+    """248320x5120 head at T_pad 32, t = 1..32 permuted: logits bits are t-invariant, sampled
+    rows are within 2 ulps of the fp64 oracle, and the block-4096 logprob of every column
+    equals the fixed-order fp32 oracle on the GPU's own logits."""
+    from tests.helpers import within_bf16_ulps
+    d = synth.head_logprob()
+    q, s, pool, targets = d["q"], d["s"], d["pool"], d["targets"]
+    Wd, Sd = i8(q), f16(s)
+    say("case head t=32 identity")
+    base_d = w8.w8_linear_invariant(Wd, Sd, bf16(pool), 32, 32)
+    base = bits(base_d)
+    rows = np.sort(np.random.default_rng(3).choice(q.shape[0], size=2048, replace=False))
+    ok, err = within_bf16_ulps(base[:, rows], oracle.w8_linear(q, s, pool, rows=rows), 2.0)
+    say(f"head sampled rows: max err {float(err.max()):.3f} ulp, {int((~ok).sum())} outside")
+    assert ok.all()
+    lp_base = host(w8.vocab_block_logprob(base_d, torch.from_numpy(targets).to(DEV), 4096))
+    want = oracle.block_logprob(base, targets, 4096)
+    assert compare(lp_base, want, "head logprob t=32") == 0
+    for t in range(1, 33):
+        cols = d["perms"][t]
+        yd = w8.w8_linear_invariant(Wd, Sd, bf16(pool[cols]), t, 32)
+        y = bits(yd)
+        assert np.array_equal(y, base[cols]), f"logits changed bits at t={t}"
+        lp = host(w8.vocab_block_logprob(yd, torch.from_numpy(targets[cols]).to(DEV), 4096))
+        assert np.array_equal(f32bits(lp), f32bits(lp_base[cols])), f"logprob changed bits at t={t}"
