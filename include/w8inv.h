@@ -70,7 +70,8 @@ const char *w8i_version(void);
  *   T_pad  fixed decode width: 16, 32, 48 or 64.  The kernel computes all
  *          T_pad columns (the first ones real, the rest zero) for every t.
  *   N      output rows, N >= 1 (any N: the last row strip is masked).
- *   K      reduction length, K >= 32 and K % 32 == 0.
+ *   K      reduction length, K >= 32 and K % 32 == 0; N * K < 2^32
+ *          (4 GiB of codes per call) and ldx <= 2^24.
  *
  * Arithmetic, fixed for every (t, T_pad, N, device):
  *   - int8 codes become bf16 exactly; each 32-element group's products are

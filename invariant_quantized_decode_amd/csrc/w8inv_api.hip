@@ -54,9 +54,9 @@ int w8_linear_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_
     if (t < 0 || t > T_pad) return W8I_ET;
     if (t == 0) return W8I_OK;
     if (!W_q || !scales || !x || !y) return W8I_ENULL;
-    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxDim * 64)
-        return W8I_ESHAPE;
-    if (ldx < K || ldy < N) return W8I_ESHAPE;
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return W8I_ESHAPE;
+    if (N * K >= ((int64_t)1 << 32)) return W8I_ESHAPE;  // per-lane 32-bit byte offsets
+    if (ldx < K || ldy < N || ldx > ((int64_t)1 << 24)) return W8I_ESHAPE;
     if (!aligned(W_q, 16) || !aligned(x, 16) || ldx % 8 != 0 || !aligned(scales, 2) || !aligned(y, 2))
         return W8I_EALIGN;
     if ((N + 31) / 32 > 0x7fffffffLL) return W8I_ESHAPE;

@@ -41,7 +41,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 32;             // output rows per workgroup (MFMA 32x32 tile)
 constexpr int kGemmThreads = 64 * kKSlices;
-constexpr int kBatch = 4;             // groups whose loads are issued together
+constexpr size_t kMaxGemmLds = 160 * 1024;  // LDS of one gfx950 workgroup
+constexpr int kMinTilesPerCu = 2;            // persistent tiles need at least this many per CU
 
 // two int8 codes (bytes 2i and 2i+1 of q) -> two bf16 in one dword, exact
 __device__ __forceinline__ uint32_t dequant2(uint32_t q, int i) {
@@ -55,34 +56,99 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q0, uint32_t q1) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int NT>  // NT = number of 32-column tiles = ceil(T_pad / 32)
+// ----------------------------------------------------------------------------
+// Loads.  A stage is two consecutive groups.  One load instruction covers 16
+// rows (or 16 activation columns) x 64 contiguous bytes, so every row segment
+// is read whole; the matrix-core layout (lane = row + 32 * half) is then
+// restored in registers with v_permlane16_swap, which exchanges lane bit 4
+// with the index of the register pair:
+//   weights     lane l of instruction i reads row 16 i + (l & 15),
+//               group (l >> 4) & 1 of the stage, 16-byte half l >> 5;
+//   activations lane l of instruction (gs, i) reads column 16 i + (l & 15),
+//               group gs, byte offset 32 (l >> 5) + 16 ((l >> 4) & 1).
+// After the swap, register pair slot 0 / 1 holds group 0 / 1 (weights) or
+// half 0 / 1 of the group (activations) in the layout the MFMA reads.
+// ----------------------------------------------------------------------------
+
+// Row stride (in 16-bit scales) of the strip's scales in LDS: at least G, and
+// an odd number of dwords, so the 32 rows read in one instruction fall in 32
+// different banks.
+__host__ __device__ __forceinline__ int scale_row_stride(int64_t G) {
+    return 2 * ((int)((G + 1) / 2) | 1);
+}
+
+__device__ __forceinline__ void swap16(u32x4& a, u32x4& b) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a[q], b[q], false, false);
+        a[q] = r[0];
+        b[q] = r[1];
+    }
+}
+
+template <int NT>
+struct Stage {
+    u32x4 w[2];          // [instruction i] -> after swap16: [group of the stage]
+    u32x4 x[NT][2][2];   // [tile][group gs][instruction i] -> after swap16: [tile][gs][half h]
+};
+
+// Ring depth in stages: every load of stage k + D is issued while stage k is
+// consumed, and all loads use the same distance because the memory counter
+// retires them in issue order.
+template <int NT>
+struct Ring {
+    static constexpr int depth = NT == 1 ? 4 : 2;
+};
+
+template <int TP16>  // T_pad / 16
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_fixed_width(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy) {
-    // slice partials travel through LDS: slot x tile-value x lane
-    __shared__ double red[kKSlices / 2][NT * 16][64];
+    constexpr int NT = (TP16 + 1) / 2;                // 32-column tiles
+    constexpr int D = Ring<NT>::depth;
+    constexpr int kLastValues = (TP16 & 1) ? 8 : 16;  // real rows of the last tile's 16 per lane
+    // LDS: the strip's scales during the main loop, then the 7 partials the
+    // left fold consumes (the two uses are separated by a barrier)
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint16_t* s_lds = reinterpret_cast<uint16_t*>(lds);
+    double* fold = reinterpret_cast<double*>(lds);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r = lane & 31;  // B column (weight row) and A row (activation column)
-    const int c = lane >> 5;  // which 16-byte half of each 32-byte group
-    const int64_t G = K / kGroup;
-    const int64_t g_begin = kslice_begin(G, wave);
-    const int64_t g_end = kslice_begin(G, wave + 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = (int)(K / kGroup);
+    const int s_stride = scale_row_stride(G);
+    const int64_t n0 = (int64_t)blockIdx.x * kRows;
 
-    const int64_t n = (int64_t)blockIdx.x * kRows + r;
-    const bool row_ok = n < N;
-    const int8_t* wp = W + (row_ok ? n : 0) * K + 16 * c;
-    const uint16_t* sp = S + (row_ok ? n : 0) * G;
+    const int g_begin = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave));
+    const int g_end = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave + 1));
 
-    const uint16_t* xp[NT];
-    bool col_ok[NT];
+    // Buffer resources: the per-lane offsets below are fixed for the whole
+    // kernel and the stage offset is a scalar.  Rows past N read row N-1,
+    // columns past t read column t-1 (valid memory, results never stored);
+    // the descriptors' ranges also bound every access.
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(N * K), 0x00020000);
+    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
+    uint32_t w_off[2];     // this lane's weight piece in group 0 of the stage
+    uint32_t w_off_gs[2];  // ... in the group it carries, (lane >> 4) & 1
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        const int j = 32 * tt + r;
-        col_ok[tt] = j < t;
-        xp[tt] = X + (col_ok[tt] ? j : 0) * ldx + 16 * c;
+    for (int i = 0; i < 2; ++i) {
+        const int64_t nr = n0 + 16 * i + (lane & 15);
+        w_off[i] = (uint32_t)((nr < N ? nr : N - 1) * K) + 16u * (lane >> 5);
+        w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
     }
+    uint32_t x_off[NT][2];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int j = 32 * tt + 16 * i + (lane & 15);
+            const int jc = j < t ? j : t - 1;
+            x_off[tt][i] = (uint32_t)(jc * ldx) * 2u + 32u * (lane >> 5) + 16u * ((lane >> 4) & 1);
+        }
+    const int r = lane & 31;  // weight row of this lane after the swaps (B column, D column)
+    const int c = lane >> 5;
 
     double acc[NT][16];
 #pragma unroll
@@ -90,93 +156,444 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_fixed_width(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[tt][v] = 0.0;
 
-    for (int64_t g = g_begin; g < g_end; g += kBatch) {
-        u32x4 wv[kBatch];
-        uint32_t sv[kBatch];
-        u32x4 xv[kBatch][NT][2];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t gg = g + u;
-            const bool ok = gg < g_end;
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            wv[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(wp + kGroup * gg) : zero;
-            sv[u] = (ok && row_ok) ? (uint32_t)sp[gg] : 0u;
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    xv[u][tt][h] = (ok && col_ok[tt])
-                                       ? *reinterpret_cast<const u32x4*>(xp[tt] + kGroup * gg + 8 * h)
-                                       : zero;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (g + u >= g_end) break;  // uniform across the workgroup's wave
-            const bf16x8 b_lo = dequant8(wv[u].x, wv[u].y);
-            const bf16x8 b_hi = dequant8(wv[u].z, wv[u].w);
-            const double s = f16_to_f64(sv[u]);
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                f32x16 d = {};
-                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv[u][tt][0]), b_lo, d,
-                                                            0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv[u][tt][1]), b_hi, d,
-                                                            0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[tt][v] = __builtin_fma(s, (double)d[v], acc[tt][v]);
-            }
-        }
-    }
+    const int len = g_end - g_begin;
+    const int full = len >> 1;  // stages with two groups of this slice
+    const int odd = len & 1;    // the row's last group when K/32 is odd (last slice only)
+    // Prefetches past the slice's last full stage are clamped to it: they
+    // re-read cached lines instead of the next slice's data.
+    const int last_full = g_begin + 2 * (full > 0 ? full - 1 : 0);
 
-    // fixed tree over the 8 slice sums: level L pairs wave w (left, receives)
-    // with wave w + 2^L (right, sends), for w a multiple of 2^(L+1).
+    // stage starting at group g: both groups lie inside the slice
+    auto load_stage = [&](int g, Stage<NT>& st) {
+        const int gc = min(g, last_full);
 #pragma unroll
-    for (int level = 0; level < 3; ++level) {
-        const int span = 1 << level;
-        const bool sender = (wave & (2 * span - 1)) == span;
-        const bool receiver = (wave & (2 * span - 1)) == 0;
-        const int slot = wave >> (level + 1);
-        if (sender) {
+        for (int i = 0; i < 2; ++i)
+            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off_gs[i], gc * kGroup, 0));
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs)
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) red[slot][tt * 16 + v][lane] = acc[tt][v];
-        }
-        __syncthreads();
-        if (receiver) {
+                for (int i = 0; i < 2; ++i)
+                    st.x[tt][gs][i] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, x_off[tt][i], (gc + gs) * (2 * kGroup), 0));
+    };
+    // the single group g in position 0 (position 1 repeats it, never consumed)
+    auto load_single = [&](int g, Stage<NT>& st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[i], g * kGroup, 0));
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs)
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[tt][v] = acc[tt][v] + red[slot][tt * 16 + v][lane];
+                for (int i = 0; i < 2; ++i)
+                    st.x[tt][gs][i] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, x_off[tt][i], g * (2 * kGroup), 0));
+    };
+    auto arrange = [&](Stage<NT>& st) {
+        swap16(st.w[0], st.w[1]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int gs = 0; gs < 2; ++gs) swap16(st.x[tt][gs][0], st.x[tt][gs][1]);
+    };
+    // one group's products, summed by the matrix core from zero
+    auto group_mfma = [&](const Stage<NT>& st, int gs, f32x16 (&d)[NT]) {
+        const bf16x8 b_lo = dequant8(st.w[gs].x, st.w[gs].y);
+        const bf16x8 b_hi = dequant8(st.w[gs].z, st.w[gs].w);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const f32x16 zero = {};
+            d[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.x[tt][gs][0]), b_lo,
+                                                            zero, 0, 0, 0);
+            d[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.x[tt][gs][1]), b_hi,
+                                                            d[tt], 0, 0, 0);
         }
-        __syncthreads();
+    };
+    // acc += s * D_g in fp64 (the product is exact there), groups ascending
+    auto step = [&](const Stage<NT>& st, int gs, int g) {
+        f32x16 d[NT];
+        group_mfma(st, gs, d);
+        const double sc = (double)(float)__builtin_bit_cast(_Float16, s_lds[r * s_stride + g]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int nv = (tt == NT - 1) ? kLastValues : 16;
+#pragma unroll
+            for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc, (double)d[tt][v], acc[tt][v]);
+        }
+    };
+
+    Stage<NT> ring[D];
+    if (full > 0) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u]);
+    }
+    // (issued after the first stages, so both latencies overlap)
+    // The strip's scales -> LDS: 16 threads per row, each taking every 16th
+    // group, 8 loads in flight at a time (rows past N read zeros from the
+    // descriptor's range check; they are never stored).
+    {
+        const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(N * G * 2), 0x00020000);
+        const int rr = threadIdx.x >> 4, c0 = threadIdx.x & 15;
+        const uint32_t row_off = (uint32_t)((n0 + rr) * G) * 2u;
+        for (int cb = c0; cb < G; cb += 16 * 8) {
+            uint16_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int col = cb + 16 * q;
+                v[q] = col < G ? __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, row_off + 2u * col, 0, 0) : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int col = cb + 16 * q;
+                if (col < G) s_lds[rr * s_stride + col] = v[q];
+            }
+        }
+    }
+    __syncthreads();
+
+    if (full > 0) {
+        int g = g_begin;
+        const int nblocks = full / D;
+        for (int blk = 0; blk < nblocks; ++blk) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                arrange(ring[u]);
+                step(ring[u], 0, g);
+                step(ring[u], 1, g + 1);
+                // keep the refill after this stage's compute: hoisting it
+                // would need a second set of stage registers
+                __builtin_amdgcn_sched_barrier(0);
+                load_stage(g + 2 * D, ring[u]);
+                __builtin_amdgcn_sched_barrier(0);
+                g += 2;
+            }
+        }
+        // the remaining full stages (fewer than D) were loaded already
+        switch (full - nblocks * D) {
+#define W8I_TAIL(R)                                     \
+    case R:                                             \
+        _Pragma("unroll") for (int u = 0; u < R; ++u) { \
+            arrange(ring[u]);                           \
+            step(ring[u], 0, g);                        \
+            step(ring[u], 1, g + 1);                    \
+            g += 2;                                     \
+        }                                               \
+        break;
+            W8I_TAIL(1)
+            W8I_TAIL(2)
+            W8I_TAIL(3)
+            W8I_TAIL(4)
+            W8I_TAIL(5)
+#undef W8I_TAIL
+            default:
+                break;
+        }
+    }
+    if (odd) {
+        Stage<NT> st;
+        load_single(g_end - 1, st);
+        arrange(st);
+        step(st, 0, g_end - 1);
     }
 
-    if (wave == 0 && row_ok) {
-        // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
-        // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns) of the tile
+    // left fold of the 8 slice sums: ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7
+    __syncthreads();  // the scales' LDS becomes the fold buffer
+    constexpr int kVals = NT * 16;
+    if (wave > 0) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v)
+                fold[((wave - 1) * kVals + tt * 16 + v) * 64 + lane] = acc[tt][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 1; w < kKSlices; ++w)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v)
+                    acc[tt][v] = acc[tt][v] + fold[((w - 1) * kVals + tt * 16 + v) * 64 + lane];
+        const int64_t n = n0 + r;
+        if (n < N) {
+            // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
+            // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns) of the tile
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
+                    const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
+                    if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(acc[tt][v]);
+                }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Large N: persistent tiles.  One workgroup per CU streams tiles of 8 strips
+// (256 rows); wave w owns strip w of the tile and walks all of K, keeping the
+// current slice's sum and the left fold of the finished slices in registers,
+// so every output gets exactly the bits of the split-K kernel above.  The
+// activation stage (2 groups x 32 columns per tile) is loaded once per
+// workgroup into a double-buffered LDS ring and read by all 8 waves.  Weight
+// and scale loads run D stages ahead across tile boundaries.
+// ----------------------------------------------------------------------------
+constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
+
+template <int NT>
+struct TileRing {
+    static constexpr int depth = NT == 1 ? 4 : 2;
+};
+
+// LDS address of the 16-byte piece p8 (0..7) of activation column a in one
+// 32-column x 128-byte stage tile: XOR swizzle so that 16 consecutive lanes
+// reading the same piece of 16 columns hit different banks.
+__device__ __forceinline__ uint32_t x_lds_off(int a, int p8) {
+    return (uint32_t)(a * 128 + 16 * (p8 ^ ((a >> 1) & 7)));
+}
+
+template <int TP16>
+__global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
+    const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, int ntiles) {
+    constexpr int NT = (TP16 + 1) / 2;
+    constexpr int D = TileRing<NT>::depth;
+    constexpr int kLastValues = (TP16 & 1) ? 8 : 16;
+    __shared__ __align__(16) unsigned char x_lds[2][NT][32 * 128];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = (int)(K / kGroup);
+    const int nst = (G + 1) >> 1;  // stages per tile (the last one holds 1 group when G is odd)
+    const int my_tiles = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int nq = my_tiles * nst;  // stages this workgroup processes
+    const int r = lane & 31, c = lane >> 5;
+
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(N * K), 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(N * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
+
+    // this wave's share of each activation stage: columns 4 w .. 4 w + 3,
+    // lane l -> column 4 w + (l >> 4), bytes 8 (l & 15) .. + 8 of the 128
+    const int xa = 4 * wave + (lane >> 4);
+    uint32_t xg_off[NT];
+    uint32_t xl_off[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        const int j = 32 * tt + xa;
+        const int jc = j < t ? j : t - 1;
+        xg_off[tt] = (uint32_t)(jc * ldx) * 2u + 8u * (lane & 15);
+        xl_off[tt] = (uint32_t)(tt * 32 * 128) + x_lds_off(xa, (lane & 15) >> 1) + 8u * (lane & 1);
+    }
+
+    struct WStage {
+        u32x4 w[2];
+        uint16_t s[2];
+        uint32_t x[NT][2];
+    };
+    // tile and stage of global stage index q (wave-uniform)
+    auto tile_of = [&](int q) { return (int)blockIdx.x + (q / nst) * (int)gridDim.x; };
+    auto load = [&](int q, WStage& st) {
+        const int qc = q < nq ? q : nq - 1;  // past the end: repeat the last stage (cached)
+        const int tile = tile_of(qc);
+        const int g = 2 * (qc % nst);
+        const int g1 = g + 1 < G ? g + 1 : g;  // odd G: the last stage repeats its group
+        const int64_t strip_row = (int64_t)tile * (kTileStrips * kRows) + (int64_t)wave * kRows;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int64_t row = strip_row + 16 * i + (lane & 15);
+            row = row < N ? row : N - 1;
+            const int gl = ((lane >> 4) & 1) ? g1 : g;
+            const uint32_t off = (uint32_t)(row * K) + (uint32_t)gl * kGroup + 16u * (lane >> 5);
+            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, off, 0, 0));
+        }
+        {
+            int64_t row = strip_row + r;
+            row = row < N ? row : N - 1;
+            const uint32_t off = (uint32_t)(row * G) * 2u;
+            st.s[0] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, off + 2u * g, 0, 0);
+            st.s[1] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, off + 2u * g1, 0, 0);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            // second group's half of the 128-byte stage row (g1 == g repeats it)
+            const uint32_t goff = (lane & 8) ? (uint32_t)g1 * 64u - 64u : (uint32_t)g * 64u;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(x_rsrc, xg_off[tt] + goff, 0, 0);
+            st.x[tt][0] = v[0];
+            st.x[tt][1] = v[1];
+        }
+    };
+    auto write_x = [&](const WStage& st, int slot) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            uint32_t* p = reinterpret_cast<uint32_t*>(&x_lds[slot][0][0] + xl_off[tt]);
+            p[0] = st.x[tt][0];
+            p[1] = st.x[tt][1];
+        }
+    };
+
+    double acc[NT][16], total[NT][16];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[tt][v] = total[tt][v] = 0.0;
+
+    WStage ring[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(u, ring[u]);
+    write_x(ring[0], 0);
+    __syncthreads();
+
+    // `slice` is the slice the next group belongs to; a slice is folded into
+    // the running total as soon as the groups before the next stage are done
+    // (empty slices, possible when K < 512, fold a +0 sum like any other).
+    int slice = 0;
+    auto fold_slice = [&]() {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
-                if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(acc[tt][v]);
+                total[tt][v] = slice == 0 ? acc[tt][v] : total[tt][v] + acc[tt][v];
+                acc[tt][v] = 0.0;
             }
+        ++slice;
+    };
+    // one stage: q is the global stage index, `cur` its ring slot and `nxt`
+    // the slot of stage q + 1 (whose activations are published now)
+    auto stage = [&](int q, WStage& cur, const WStage& nxt) {
+        write_x(nxt, (q + 1) & 1);
+        swap16(cur.w[0], cur.w[1]);
+        const int g = 2 * (q % nst);
+        const int ng = (g + 1 < G) ? 2 : 1;
+        if (kslice_begin(G, slice + 1) <= g) {
+            do fold_slice();
+            while (kslice_begin(G, slice + 1) <= g);
+        }
+        const unsigned char* xs = &x_lds[q & 1][0][0];
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs) {
+            if (gs >= ng) break;  // odd G: the tile's last stage has one group
+            const bf16x8 b_lo = dequant8(cur.w[gs].x, cur.w[gs].y);
+            const bf16x8 b_hi = dequant8(cur.w[gs].z, cur.w[gs].w);
+            const double sc = (double)(float)__builtin_bit_cast(_Float16, cur.s[gs]);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const u32x4 a0 =
+                    *reinterpret_cast<const u32x4*>(xs + tt * 32 * 128 + x_lds_off(r, 4 * gs + 2 * c));
+                const u32x4 a1 =
+                    *reinterpret_cast<const u32x4*>(xs + tt * 32 * 128 + x_lds_off(r, 4 * gs + 2 * c + 1));
+                const f32x16 zero = {};
+                f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo, zero, 0,
+                                                                   0, 0);
+                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
+                const int nv = (tt == NT - 1) ? kLastValues : 16;
+#pragma unroll
+                for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc, (double)d[v], acc[tt][v]);
+            }
+        }
+        if (g + ng == G) {
+            // the tile's last stage: fold the remaining slices, store this strip
+            while (slice < kKSlices) fold_slice();
+            const int64_t n = (int64_t)tile_of(q) * (kTileStrips * kRows) + (int64_t)wave * kRows + r;
+            if (n < N) {
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
+                        const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
+                        if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(total[tt][v]);
+                    }
+            }
+            slice = 0;
+        }
+        load(q + D, cur);
+        __syncthreads();
+    };
+
+    // full blocks of D stages (no exits inside, so the wait counts stay
+    // exact), then the remaining stages
+    const int nblocks = nq / D;
+    int q = 0;
+    for (int blk = 0; blk < nblocks; ++blk, q += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) stage(q + u, ring[u], ring[(u + 1) % D]);
     }
+    switch (nq - nblocks * D) {
+#define W8I_TILE_TAIL(R)                                                         \
+    case R:                                                                      \
+        _Pragma("unroll") for (int u = 0; u < R; ++u) stage(q + u, ring[u], ring[(u + 1) % D]); \
+        break;
+        W8I_TILE_TAIL(1)
+        W8I_TILE_TAIL(2)
+        W8I_TILE_TAIL(3)
+#undef W8I_TILE_TAIL
+        default:
+            break;
+    }
+}
+
+// dynamic LDS of one workgroup: max(scales, fold partials)
+static size_t gemm_lds_bytes(int64_t K, int NT) {
+    const int64_t G = K / kGroup;
+    const size_t scales = (size_t)kRows * scale_row_stride(G) * 2;
+    const size_t partials = (size_t)(kKSlices - 1) * NT * 16 * 64 * sizeof(double);
+    return scales > partials ? scales : partials;
+}
+
+// Tiles of the persistent kernel; it is used when there are enough of them
+// to keep every CU busy for several tiles.
+static int tile_count(int64_t N) { return (int)((N + kTileStrips * kRows - 1) / (kTileStrips * kRows)); }
+
+static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
+                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return W8I_EHIP;
+    const int ntiles = tile_count(N);
+    const dim3 grid((unsigned)(ntiles < ncu ? ntiles : ncu)), block(kGemmThreads);
+    switch (T_pad / 16) {
+        case 1:
+            hipLaunchKernelGGL(gemm_w8g32_tiles<1>, grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, ntiles);
+            break;
+        case 2:
+            hipLaunchKernelGGL(gemm_w8g32_tiles<2>, grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, ntiles);
+            break;
+        default:
+            return W8I_ET;
+    }
+    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                   int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256)
+        return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, stream);
     const dim3 grid((unsigned)((N + kRows - 1) / kRows));
     const dim3 block(kGemmThreads);
-    const int NT = (T_pad + 31) / 32;
-    switch (NT) {
+    const int NT = (T_pad / 16 + 1) / 2;
+    const size_t lds = gemm_lds_bytes(K, NT);
+    if (lds > kMaxGemmLds) return W8I_ESHAPE;
+    switch (T_pad / 16) {
         case 1:
-            hipLaunchKernelGGL(gemm_w8g32_fixed_width<1>, grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy);
+            hipLaunchKernelGGL(gemm_w8g32_fixed_width<1>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
             break;
         case 2:
-            hipLaunchKernelGGL(gemm_w8g32_fixed_width<2>, grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy);
+            hipLaunchKernelGGL(gemm_w8g32_fixed_width<2>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
+            break;
+        case 3:
+            hipLaunchKernelGGL(gemm_w8g32_fixed_width<3>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
+            break;
+        case 4:
+            hipLaunchKernelGGL(gemm_w8g32_fixed_width<4>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
             break;
         default:
             return W8I_ET;

@@ -12,10 +12,12 @@ namespace w8i {
 constexpr int kGroup = 32;   // K elements per fp16 scale (W8G32)
 constexpr int kKSlices = 8;  // fixed number of K-slices per output, for every shape
 
-// First group of K-slice i when K holds G groups: floor(G * i / 8).  The
-// whole K-reduction plan is this function of K alone.
+// First group of K-slice i when K holds G groups.  Slices are made of whole
+// pairs of groups: slice i covers pairs [floor(P*i/8), floor(P*(i+1)/8)),
+// P = G/2, and when G is odd the row's last group closes slice 7.  The whole
+// K-reduction plan is this function of K alone.
 __host__ __device__ __forceinline__ int64_t kslice_begin(int64_t G, int i) {
-    return (G * i) / kKSlices;
+    return i >= kKSlices ? G : 2 * (((G / 2) * i) / kKSlices);
 }
 
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,

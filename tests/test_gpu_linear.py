@@ -204,3 +204,30 @@ def test_mlp_projections_t_values():
             cols = d["perms"][t]
             y = run(Wd, Sd, bf16(pool[cols]), t, 64)
             assert np.array_equal(y, base[cols]), f"{key}: bits changed at t={t}"
+
+
+# ------------------------------------------------- large N (persistent tile kernel)
+LARGE = [  # N, K, T_pad: N >= 131072 selects the persistent kernel for T_pad <= 32
+    (131072 + 100, 1024, 32),
+    (131072 + 33, 96, 16),      # K/32 = 3: odd group count, seven empty slices
+    (131072 + 256, 5120, 32),
+]
+
+
+@pytest.mark.parametrize("N,K,T_pad", LARGE)
+def test_large_n_matches_row_slices_and_oracle(N, K, T_pad):
+    """The persistent mapping and the split-K mapping (row slices run as their own, smaller
+    problems) give the same bits; sampled rows are within 2 ulps of the oracle."""
+    rng = np.random.default_rng(N + K)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    x = synth.draw_acts(rng, T_pad, K)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    for t in (1, 7, T_pad):
+        say(f"case large N={N} K={K} T_pad={T_pad} t={t}")
+        full = run(Wd, Sd, Xd[:t], t, T_pad)
+        for r0, r1 in ((0, 544), (N - 300, N), (65536 + 17, 65536 + 17 + 1000)):
+            part = run(Wd[r0:r1], Sd[r0:r1], Xd[:t], t, T_pad)
+            assert np.array_equal(part, full[:, r0:r1]), f"rows {r0}:{r1} differ at t={t}"
+        rows = np.sort(np.concatenate([rng.choice(N, size=512, replace=False), [0, N - 1]]))
+        check_parity(full[:, rows], oracle.w8_linear(q, s, x[:t], rows=rows), f"large N={N} K={K} t={t}")
