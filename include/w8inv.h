@@ -77,10 +77,12 @@ const char *w8i_version(void);
  *   - int8 codes become bf16 exactly; each 32-element group's products are
  *     summed by bf16 matrix-core instructions into fp32 starting from zero;
  *   - that group sum is multiplied by its fp16 scale and accumulated in fp64;
- *   - K is cut into 8 contiguous slices of whole groups, slice i covering
- *     groups [floor(G*i/8), floor(G*(i+1)/8)), G = K/32; each slice is summed
- *     in ascending group order and the 8 slice sums are combined by the fixed
- *     tree ((0+1)+(2+3))+((4+5)+(6+7)).  The plan depends on K only;
+ *   - K is cut into 8 contiguous slices of whole pairs of groups: with
+ *     G = K/32 groups and P = floor(G/2) pairs, slice i covers groups
+ *     [2*floor(P*i/8), 2*floor(P*(i+1)/8)) and, when G is odd, slice 7 also
+ *     takes the last group.  Each slice is summed in ascending group order
+ *     (an empty slice is +0) and the 8 slice sums are combined by the left
+ *     fold ((((((s0+s1)+s2)+s3)+s4)+s5)+s6)+s7.  The plan depends on K only;
  *   - the fp64 result is rounded once to bf16, nearest-even.
  *   No atomics, no autotuning, no choice made from t.
  *

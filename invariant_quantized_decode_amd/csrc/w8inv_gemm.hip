@@ -9,19 +9,23 @@
 // arithmetic", row "ops::linear W8G32".
 //
 // Design for gfx950 (CDNA4):
-//  * One workgroup = one strip of 32 output rows x all K.  Its 8 waves take
-//    the 8 fixed K-slices (slice i = groups [G*i/8, G*(i+1)/8), G = K/32).
-//  * Per 32-element group, each lane loads 16 contiguous weight bytes of its
-//    row (row = lane % 32, half = lane / 32) with one 128-bit load; the two
-//    8-byte halves feed the B operand of two chained
-//    v_mfma_f32_32x32x16_bf16 (A = activations, B = weights), so one group's
-//    32 products per output are summed by the matrix core into fp32 from
-//    zero.  The same K permutation is applied to the activations.
-//  * int8 -> bf16 is exact (7 significant bits); the fp16 group scale is
-//    applied afterwards in fp64 (the product is exact there) and the groups
-//    are accumulated in fp64 in ascending order inside each slice.
-//  * The 8 slice sums meet in LDS in the fixed tree ((0+1)+(2+3))+((4+5)+(6+7)),
-//    then wave 0 rounds to bf16 once and stores the real columns.
+//  * The K plan is a function of K alone: 8 contiguous K-slices made of whole
+//    pairs of 32-element groups (kslice_begin), each summed in ascending
+//    group order in fp64, the 8 slice sums combined by a left fold.  Two
+//    kernels run this same plan and give the same bits for every row:
+//    - gemm_w8g32_fixed_width: one workgroup = 32 output rows x all K, its 8
+//      waves take the 8 slices; slice sums meet in LDS, wave 0 folds them.
+//    - gemm_w8g32_tiles (large N, T_pad <= 32): persistent workgroups stream
+//      256-row tiles; each wave owns a 32-row strip and walks all of K,
+//      keeping the running slice sum and the fold in registers, while the
+//      activation stage is shared through a double-buffered LDS ring.
+//  * Loads are coalesced: one instruction covers 16 rows x 64 contiguous
+//    bytes (two groups); v_permlane16_swap restores the matrix-core layout.
+//    Each group's 32 products per output are summed by two chained
+//    v_mfma_f32_32x32x16_bf16 (A = activations, B = weights) into fp32 from
+//    zero; int8 -> bf16 is exact (7 significant bits).
+//  * The fp16 group scale is applied to that fp32 group sum in fp64 (the
+//    product is exact there); the fp64 result is rounded once to bf16.
 //  * Every one of the T_pad columns goes through the matrix core for every t;
 //    columns >= t are zero registers, never loaded and never stored.
 //  * No atomics; nothing depends on t, T_pad, N or the device.
@@ -335,6 +339,236 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_fixed_width(
 }
 
 // ----------------------------------------------------------------------------
+// T_pad <= 32: the same split-K schedule with the activations and the scales
+// staged in LDS by direct loads (buffer_load ... lds).  Every wave re-reads
+// its slice's activations from L2, and what that costs is the number of cache
+// lines touched, not the bytes: each direct load covers 8 columns x 128 bytes
+// (whole lines) and lands in a per-wave LDS ring of depth D, from which the
+// matrix-core operands are read.  The strip's scales (rows n0 .. n0+31) are
+// one contiguous block of 64 G bytes and are copied to LDS before the main
+// loop.  The arithmetic, and so every bit, is that of the kernel above.
+// ----------------------------------------------------------------------------
+#define W8I_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kXStageBytes = 32 * 128;                    // 32 columns x one stage of bf16
+constexpr int kXSlotBytes = kKSlices * kXStageBytes;      // one ring slot of all 8 waves
+constexpr int kLdsDmaBytes = 1024;                        // bytes of one wave-wide 16-byte direct load
+
+// LDS capacity left for the scales when the ring has D slots
+__host__ __device__ constexpr int split_lds_scale_bytes(int D) {
+    return (int)kMaxGemmLds - D * kXSlotBytes - (4 - D) * 16;
+}
+
+// Byte offset of 16-byte piece p (0..7) of column a inside a wave's stage:
+// XOR swizzle, so that 8 consecutive columns reading one piece hit 8
+// different bank groups.  Direct load i, lane l fills bytes 16 l .. 16 l + 15
+// of the instruction's kilobyte, which is column 8 i + (l >> 3), piece
+// (l & 7) ^ ((l >> 3) & 7).
+__device__ __forceinline__ uint32_t xs_off(int a, int p) { return (uint32_t)(a * 128 + 16 * (p ^ (a & 7))); }
+
+// s_waitcnt that waits until at most n vector-memory operations are pending
+#define W8I_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+template <int TP16, int D>  // TP16 = T_pad / 16 (1 or 2), D = ring depth in stages (2..4)
+__global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
+    const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy) {
+    static_assert(TP16 == 1 || TP16 == 2, "one 32-column tile");
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    constexpr int kLastValues = TP16 == 1 ? 8 : 16;
+    constexpr int kScaleBytes = split_lds_scale_bytes(D);
+    constexpr int kLoadsPerStage = 2 + 4;  // weight loads + direct activation loads
+    // one array per ring slot, so the compiler can wait for each slot's loads alone
+    __shared__ __align__(16) unsigned char xr0[kXSlotBytes];
+    __shared__ __align__(16) unsigned char xr1[kXSlotBytes];
+    __shared__ __align__(16) unsigned char xr2[D > 2 ? kXSlotBytes : 16];
+    __shared__ __align__(16) unsigned char xr3[D > 3 ? kXSlotBytes : 16];
+    __shared__ __align__(16) unsigned char s_raw[kScaleBytes];
+    const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(s_raw);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = (int)(K / kGroup);
+    const int64_t n0 = (int64_t)blockIdx.x * kRows;
+    const int g_begin = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave));
+    const int g_end = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave + 1));
+
+    // Rows past N read row N-1 and columns past t read column t-1 (valid
+    // memory, results never stored); the descriptors' ranges bound every access.
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(N * K), 0x00020000);
+    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
+    // The range is rounded up to whole 16-byte pieces: a piece that straddles
+    // the end would otherwise come back as zeros, scales of the last row
+    // included.  S is 16-byte aligned here, so the rounded piece lies in the
+    // same aligned 16 bytes (and page) as the last scales.
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(S), (short)0, (int)(((uint32_t)(N * G * 2) + 15u) & ~15u), 0x00020000);
+
+    // the strip's scales -> LDS, issued first so the wait below can leave the
+    // activation ring in flight
+    const int s_loads = (64 * G + kLdsDmaBytes - 1) / kLdsDmaBytes;
+    for (int k = wave; k < s_loads; k += kKSlices)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, W8I_LDS(s_raw + k * kLdsDmaBytes), 16, 16u * lane,
+                                                 (uint32_t)(n0 * G * 2) + (uint32_t)(k * kLdsDmaBytes), 0, 0);
+
+    uint32_t w_off[2];     // this lane's weight piece in group 0 of the stage
+    uint32_t w_off_gs[2];  // ... in the group it carries, (lane >> 4) & 1
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t nr = n0 + 16 * i + (lane & 15);
+        w_off[i] = (uint32_t)((nr < N ? nr : N - 1) * K) + 16u * (lane >> 5);
+        w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
+    }
+    uint32_t xd_off[4];  // direct load i of a stage: columns 8 i .. 8 i + 7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int a = 8 * i + (lane >> 3);
+        const int jc = a < t ? a : t - 1;
+        xd_off[i] = (uint32_t)(jc * ldx) * 2u + 16u * ((lane & 7) ^ ((lane >> 3) & 7));
+    }
+    const int r = lane & 31;  // weight row of this lane after the swaps (B column, D column)
+    const int c = lane >> 5;
+    // matrix-core A operand: lane (r, c) takes K [16 c, 16 c + 16) of group gs
+    // of column r = pieces 4 gs + 2 c (first MFMA) and 4 gs + 2 c + 1 (second)
+    uint32_t xa_off[2][2];
+#pragma unroll
+    for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xa_off[gs][h] = (uint32_t)(wave * kXStageBytes) + xs_off(r, 4 * gs + 2 * c + h);
+
+    double acc[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0;
+
+    const int len = g_end - g_begin;
+    const int full = len >> 1;
+    const int odd = len & 1;
+    const int last_full = g_begin + 2 * (full > 0 ? full - 1 : 0);
+
+    auto slot = [&](int u) -> unsigned char* { return u == 0 ? xr0 : u == 1 ? xr1 : u == 2 ? xr2 : xr3; };
+    // stage starting at group g (clamped to the slice's last full stage);
+    // `single` loads group g alone in position 0 (the odd last group)
+    auto load_stage = [&](int g, u32x4 (&w)[2], unsigned char* xs, bool single) {
+        const int gc = single ? g : min(g, last_full);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 w_rsrc, single ? w_off[i] : w_off_gs[i], gc * kGroup, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, W8I_LDS(xs + wave * kXStageBytes + i * kLdsDmaBytes),
+                                                     16, xd_off[i], gc * (2 * kGroup), 0, 0);
+    };
+    // group gs of the stage (weights already swapped), acc += s * D_g in fp64
+    auto step = [&](const u32x4 (&w)[2], const unsigned char* xs, int gs, int g) {
+        const bf16x8 b_lo = dequant8(w[gs].x, w[gs].y);
+        const bf16x8 b_hi = dequant8(w[gs].z, w[gs].w);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + xa_off[gs][0]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + xa_off[gs][1]);
+        const f32x16 zero = {};
+        f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo, zero, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
+        const double sc = (double)(float)__builtin_bit_cast(_Float16, s_lds[r * G + g]);
+#pragma unroll
+        for (int v = 0; v < kLastValues; ++v) acc[v] = __builtin_fma(sc, (double)d[v], acc[v]);
+    };
+
+    u32x4 ring[D][2];
+    if (full > 0) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u], slot(u), false);
+        W8I_WAIT_VM(kLoadsPerStage * D);  // this wave's scale loads have landed
+    } else {
+        W8I_WAIT_VM(0);
+    }
+    // Every wave's scale loads have landed.  A plain barrier: __syncthreads()
+    // would also wait for the activation ring's loads (its release fence
+    // covers all pending LDS writes).  The signal fences keep the compiler
+    // from moving LDS accesses across it.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    int g = g_begin;
+    if (full > 0) {
+        const int nblocks = full / D;
+        for (int blk = 0; blk < nblocks; ++blk) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                swap16(ring[u][0], ring[u][1]);
+                step(ring[u], slot(u), 0, g);
+                step(ring[u], slot(u), 1, g + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                load_stage(g + 2 * D, ring[u], slot(u), false);
+                __builtin_amdgcn_sched_barrier(0);
+                g += 2;
+            }
+        }
+        switch (full - nblocks * D) {
+#define W8I_SPLIT_TAIL(R)                               \
+    case R:                                             \
+        _Pragma("unroll") for (int u = 0; u < R; ++u) { \
+            swap16(ring[u][0], ring[u][1]);             \
+            step(ring[u], slot(u), 0, g);               \
+            step(ring[u], slot(u), 1, g + 1);           \
+            g += 2;                                     \
+        }                                               \
+        break;
+            W8I_SPLIT_TAIL(1)
+            W8I_SPLIT_TAIL(2)
+            W8I_SPLIT_TAIL(3)
+#undef W8I_SPLIT_TAIL
+            default:
+                break;
+        }
+    }
+    if (odd) {
+        // the row's last group (slice 7 when K/32 is odd); the ring is drained
+        // and slot 0's region of this wave is free
+        u32x4 w1[2];
+        load_stage(g_end - 1, w1, xr0, true);
+        W8I_WAIT_VM(0);
+        swap16(w1[0], w1[1]);
+        step(w1, xr0, 0, g_end - 1);
+    }
+
+    // left fold of the 8 slice sums: ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7;
+    // the partials of waves 1..7 go to ring slots 0 and 1 (8 KB each).  The
+    // barrier's fence also waits for the clamped prefetches past the slice
+    // end, which still write into the ring.
+    __syncthreads();
+    auto fold_of = [&](int w) {
+        return reinterpret_cast<double*>((w <= 4 ? xr0 : xr1) + ((w - 1) & 3) * (16 * 64 * 8));
+    };
+    if (wave > 0) {
+        double* f = fold_of(wave);
+#pragma unroll
+        for (int v = 0; v < kLastValues; ++v) f[v * 64 + lane] = acc[v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 1; w < kKSlices; ++w) {
+            const double* f = fold_of(w);
+#pragma unroll
+            for (int v = 0; v < kLastValues; ++v) acc[v] = acc[v] + f[v * 64 + lane];
+        }
+        const int64_t n = n0 + r;
+        if (n < N) {
+            // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
+            // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns)
+#pragma unroll
+            for (int v = 0; v < kLastValues; ++v) {
+                const int j = 8 * (v >> 2) + 4 * c + (v & 3);
+                if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(acc[v]);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // Large N: persistent tiles.  One workgroup per CU streams tiles of 8 strips
 // (256 rows); wave w owns strip w of the tile and walks all of K, keeping the
 // current slice's sum and the left fold of the finished slices in registers,
@@ -579,6 +813,24 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
         return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, stream);
     const dim3 grid((unsigned)((N + kRows - 1) / kRows));
     const dim3 block(kGemmThreads);
+    // T_pad <= 32 with the strip's scales loadable as 16-byte pieces: the
+    // LDS-staged variant, with the deepest ring whose LDS leaves room for them
+    const int64_t s_bytes = (64 * (K / kGroup) + kLdsDmaBytes - 1) / kLdsDmaBytes * kLdsDmaBytes;
+    if (T_pad <= 32 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {
+        const int tp = T_pad / 16;
+#define W8I_SPLIT_LAUNCH(D)                                                                                  \
+    if (s_bytes <= split_lds_scale_bytes(D)) {                                                               \
+        if (tp == 1)                                                                                         \
+            hipLaunchKernelGGL((gemm_w8g32_split_lds<1, D>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy); \
+        else                                                                                                 \
+            hipLaunchKernelGGL((gemm_w8g32_split_lds<2, D>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy); \
+        return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;                                          \
+    }
+        W8I_SPLIT_LAUNCH(4)
+        W8I_SPLIT_LAUNCH(3)
+        W8I_SPLIT_LAUNCH(2)
+#undef W8I_SPLIT_LAUNCH
+    }
     const int NT = (T_pad / 16 + 1) / 2;
     const size_t lds = gemm_lds_bytes(K, NT);
     if (lds > kMaxGemmLds) return W8I_ESHAPE;

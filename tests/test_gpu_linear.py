@@ -187,6 +187,46 @@ def test_t_pad_and_row_slice_independence():
     assert np.array_equal(sl, a[:, r0:r1])
 
 
+# --------------------------------- the LDS-staged split-K variants (T_pad <= 32)
+STAGING = [  # N, K, t, T_pad: LDS ring depth 4 / 3 / 2 by the strip's scale bytes, then the register path
+    (257, 1056, 32, 32),   # K/32 = 33 (odd), depth 4
+    (40, 17408, 5, 32),    # K/32 = 544, depth 3
+    (24, 36896, 3, 16),    # K/32 = 1153 (odd), depth 2
+    (16, 64000, 16, 16),   # K/32 = 2000: scales too large for the ring variants
+]
+
+
+@pytest.mark.parametrize("N,K,t,T_pad", STAGING)
+def test_staging_variants_match_oracle_and_row_slices(N, K, t, T_pad):
+    say(f"case staging N={N} K={K} t={t} T_pad={T_pad}")
+    q, s, x = synth.small_linear(N + K + T_pad, N, K, t, 0.0)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    y = run(Wd, Sd, Xd, t, T_pad)
+    check_parity(y, oracle.w8_linear(q, s, x), f"staging N={N} K={K} t={t}")
+    part = run(Wd[3:], Sd[3:], Xd, t, T_pad)
+    assert np.array_equal(part, y[:, 3:]), "row slice differs"
+
+
+@pytest.mark.parametrize("T_pad", [16, 32])
+def test_unaligned_scales_give_the_same_bits(T_pad):
+    """Scales that are not 16-byte aligned cannot be copied to LDS in 16-byte pieces and take
+    the register-staged kernel; the arithmetic, and so every bit, is the same."""
+    N, K = 300, 5120
+    q, s, x = synth.small_linear(77 + T_pad, N, K, T_pad, 0.0)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    G = K // 32
+    flat = torch.zeros(N * G + 8, dtype=torch.int16, device=Sd.device)
+    Smis = flat[1:1 + N * G].view(N, G)
+    Smis.copy_(Sd)
+    assert Smis.data_ptr() % 16 == 2
+    for t in (1, T_pad):
+        say(f"case unaligned scales T_pad={T_pad} t={t}")
+        a = run(Wd, Sd, Xd[:t], t, T_pad)
+        b = run(Wd, Smis, Xd[:t], t, T_pad)
+        assert np.array_equal(a, b), f"aligned and unaligned scales differ at t={t}"
+    check_parity(a, oracle.w8_linear(q, s, x), f"unaligned-scales case T_pad={T_pad}")
+
+
 @pytest.mark.slow
 def test_mlp_projections_t_values():
     """gate/up 34816x5120 and down 5120x17408 at T_pad 64, t in {1,5,17,24,32,48,64}."""
