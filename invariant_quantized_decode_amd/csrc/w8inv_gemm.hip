@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "w8inv_internal.h"
 #include "w8inv_math.h"
 
@@ -447,19 +449,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int odd = len & 1;
     const int last_full = g_begin + 2 * (full > 0 ? full - 1 : 0);
 
+    // Prefetches past the slice's last full stage keep the loop free of
+    // branches; they go through descriptors with an empty range, which return
+    // zeros without touching memory (the slot they fill is never read).
+    const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t x_none =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, 0, 0x00020000);
+
     auto slot = [&](int u) -> unsigned char* { return u == 0 ? xr0 : u == 1 ? xr1 : u == 2 ? xr2 : xr3; };
-    // stage starting at group g (clamped to the slice's last full stage);
-    // `single` loads group g alone in position 0 (the odd last group)
+    // stage starting at group g; `single` loads group g alone in position 0
+    // (the odd last group)
     auto load_stage = [&](int g, u32x4 (&w)[2], unsigned char* xs, bool single) {
-        const int gc = single ? g : min(g, last_full);
+        const bool live = single || g <= last_full;
+        const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
+        const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 w_rsrc, single ? w_off[i] : w_off_gs[i], gc * kGroup, 0));
+                                                 wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, W8I_LDS(xs + wave * kXStageBytes + i * kLdsDmaBytes),
-                                                     16, xd_off[i], gc * (2 * kGroup), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, W8I_LDS(xs + wave * kXStageBytes + i * kLdsDmaBytes), 16,
+                                                     xd_off[i], g * (2 * kGroup), 0, 0);
     };
     // group gs of the stage (weights already swapped), acc += s * D_g in fp64
     auto step = [&](const u32x4 (&w)[2], const unsigned char* xs, int gs, int g) {
@@ -494,9 +505,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     int g = g_begin;
     if (full > 0) {
         const int nblocks = full / D;
+        // Stage q's loads are complete once only the D - 1 later stages'
+        // loads are pending.  The wait is explicit: the compiler's own
+        // tracking of direct-to-LDS loads is not relied on.
         for (int blk = 0; blk < nblocks; ++blk) {
 #pragma unroll
             for (int u = 0; u < D; ++u) {
+                W8I_WAIT_VM(kLoadsPerStage * (D - 1));
                 swap16(ring[u][0], ring[u][1]);
                 step(ring[u], slot(u), 0, g);
                 step(ring[u], slot(u), 1, g + 1);
@@ -506,22 +521,26 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
                 g += 2;
             }
         }
+        // the remaining full stages (fewer than D) were loaded already; after
+        // the u-th of them only D - 1 - u stages' loads are pending
+        auto tail_stage = [&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if constexpr (u <= D - 2) {  // a tail has at most D - 1 stages
+                W8I_WAIT_VM(kLoadsPerStage * (D - 1 - u));
+                swap16(ring[u][0], ring[u][1]);
+                step(ring[u], slot(u), 0, g);
+                step(ring[u], slot(u), 1, g + 1);
+                g += 2;
+            }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
         switch (full - nblocks * D) {
-#define W8I_SPLIT_TAIL(R)                               \
-    case R:                                             \
-        _Pragma("unroll") for (int u = 0; u < R; ++u) { \
-            swap16(ring[u][0], ring[u][1]);             \
-            step(ring[u], slot(u), 0, g);               \
-            step(ring[u], slot(u), 1, g + 1);           \
-            g += 2;                                     \
-        }                                               \
-        break;
-            W8I_SPLIT_TAIL(1)
-            W8I_SPLIT_TAIL(2)
-            W8I_SPLIT_TAIL(3)
-#undef W8I_SPLIT_TAIL
-            default:
-                break;
+            case 1: tail_stage(I0{}); break;
+            case 2: tail_stage(I0{}); tail_stage(I1{}); break;
+            case 3: tail_stage(I0{}); tail_stage(I1{}); tail_stage(I2{}); break;
+            default: break;
         }
     }
     if (odd) {
@@ -534,37 +553,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         step(w1, xr0, 0, g_end - 1);
     }
 
-    // left fold of the 8 slice sums: ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7;
-    // the partials of waves 1..7 go to ring slots 0 and 1 (8 KB each).  The
-    // barrier's fence also waits for the clamped prefetches past the slice
-    // end, which still write into the ring.
+    // Left fold of the 8 slice sums, ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7,
+    // shared by the waves: every slice sum goes to ring slots 0 and 1 (8 KB
+    // per wave), then wave w folds and stores values v = w, w + 8 of every
+    // lane.  The barrier's fence also waits for the prefetches past the slice
+    // ends, which still write into the ring.
     __syncthreads();
-    auto fold_of = [&](int w) {
-        return reinterpret_cast<double*>((w <= 4 ? xr0 : xr1) + ((w - 1) & 3) * (16 * 64 * 8));
-    };
-    if (wave > 0) {
-        double* f = fold_of(wave);
+    auto part_of = [&](int w) { return reinterpret_cast<double*>((w < 4 ? xr0 : xr1) + (w & 3) * (16 * 64 * 8)); };
+    {
+        double* f = part_of(wave);
 #pragma unroll
         for (int v = 0; v < kLastValues; ++v) f[v * 64 + lane] = acc[v];
     }
     __syncthreads();
-    if (wave == 0) {
+    const int64_t n = n0 + r;
 #pragma unroll
-        for (int w = 1; w < kKSlices; ++w) {
-            const double* f = fold_of(w);
+    for (int k = 0; k < kLastValues / kKSlices; ++k) {
+        const int v = wave + kKSlices * k;
+        double sum = part_of(0)[v * 64 + lane];
 #pragma unroll
-            for (int v = 0; v < kLastValues; ++v) acc[v] = acc[v] + f[v * 64 + lane];
-        }
-        const int64_t n = n0 + r;
-        if (n < N) {
-            // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
-            // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns)
-#pragma unroll
-            for (int v = 0; v < kLastValues; ++v) {
-                const int j = 8 * (v >> 2) + 4 * c + (v & 3);
-                if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(acc[v]);
-            }
-        }
+        for (int w = 1; w < kKSlices; ++w) sum = sum + part_of(w)[v * 64 + lane];
+        // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
+        // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns)
+        const int j = 8 * (v >> 2) + 4 * c + (v & 3);
+        if (n < N && j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(sum);
     }
 }
 
