@@ -138,7 +138,7 @@ int vocab_block_logprob(const uint16_t *logits, const int64_t *targets, int32_t 
  * Column-local glue between the projections of one decode layer.  The ninfer
  * issue's "Where t selects arithmetic" notes that norms and other per-lane
  * ops are invariant; these kernels keep every column's arithmetic independent
- * of the other columns.  bf16 in and out, fp32 arithmetic, bf16 rounding
+ * of the other columns.  bf16 in and out, fp32 arithmetic (SwiGLU: fp64), bf16 rounding
  * nearest-even.  Pointers 2-byte aligned.
  *
  * w8i_rmsnorm: y[j,:] = x[j,:] * w / sqrt(mean(x[j,:]^2) + eps), w = weight
@@ -147,7 +147,9 @@ int vocab_block_logprob(const uint16_t *logits, const int64_t *targets, int32_t 
  *   then mean = sum / H, d = sqrt(mean + eps), y = (x / d) * w, each one
  *   correctly rounded fp32 operation.  1 <= H <= 65536.
  * w8i_swiglu: y[j,h] = silu(g) * u with g = gate_up[j,h], u = gate_up[j,F+h]:
- *   silu(g) = g / (1 + EXP32(-g)), fp32.
+ *   silu(g) = g / (1 + e^-g), evaluated in fp64 (e^x by the device library's
+ *   fp64 exp) and rounded once to bf16; fp32 would overflow e^-g for g < -88.7
+ *   where g e^g u can still be a normal bf16.
  * w8i_residual_add: y[j,h] = a[j,h] + b[j,h] in fp32, rounded to bf16
  *   (y may alias a or b).
  * ------------------------------------------------------------------------- */

@@ -62,10 +62,13 @@ __global__ void swiglu_kernel(const uint16_t* __restrict__ gu, uint16_t* __restr
     const int j = blockIdx.y;
     const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (h >= F) return;
-    const float g = bf16_to_f32(gu[(int64_t)j * ldg + h]);
-    const float u = bf16_to_f32(gu[(int64_t)j * ldg + F + h]);
-    const float silu = g / (1.0f + exp32(-g));
-    y[(int64_t)j * ldy + h] = f32_to_bf16(silu * u);
+    // fp64: e^-g of any bf16 gate is finite or its silu is below bf16's range,
+    // so the only rounding that matters is the final one to bf16 (in fp32,
+    // e^-g overflows for g < -88.7 while g e^g u can still be a normal bf16)
+    const double g = (double)bf16_to_f32(gu[(int64_t)j * ldg + h]);
+    const double u = (double)bf16_to_f32(gu[(int64_t)j * ldg + F + h]);
+    const double silu = g / (1.0 + ::exp(-g));
+    y[(int64_t)j * ldy + h] = f64_to_bf16(silu * u);
 }
 
 __global__ void residual_add_kernel(const uint16_t* a, const uint16_t* b, uint16_t* y, int64_t H, int64_t lda,
