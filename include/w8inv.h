@@ -96,6 +96,13 @@ int w8_linear_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_
                         int64_t N, int64_t K, int64_t ldx, int64_t ldy,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Name of the kernel that w8_linear_invariant runs for these arguments (static
+ * storage; "" for arguments it would reject), for matching profiler records.
+ * The choice depends on N, K, T_pad and on whether `scales` is 16-byte
+ * aligned -- never on t -- and every kernel runs the K plan above, so it
+ * changes no bit of the result.  Pure host function: no device access. */
+const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t *scales);
+
 /* ---------------------------------------------------------------------------
  * Target-token logprob by fixed-width vocabulary blocks (LM-head epilogue).
  *

@@ -25,7 +25,7 @@ STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: 
           -6: "W8I_EWORKSPACE", -7: "W8I_EHIP"}
 
 EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
-           "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
+           "w8_linear_invariant_kernel", "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32")
 
 
@@ -46,6 +46,7 @@ def _load():
     L.w8_linear_invariant_workspace_bytes.restype = SZ
     L.w8_linear_invariant.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
     L.w8_linear_invariant.restype = ctypes.c_int
+    L.w8_linear_invariant_kernel.argtypes, L.w8_linear_invariant_kernel.restype = [I64, I64, I32, P], ctypes.c_char_p
     L.vocab_block_logprob_workspace_bytes.argtypes = [I32, I64, I32]
     L.vocab_block_logprob_workspace_bytes.restype = SZ
     L.vocab_block_logprob.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
@@ -135,6 +136,13 @@ def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor
                                   None, 0, ctypes.c_void_p(_stream(W_q.device)))
     _check("w8_linear_invariant", st)
     return y
+
+
+def w8_linear_invariant_kernel(N: int, K: int, T_pad: int, scales: torch.Tensor | None = None) -> str:
+    """Name of the kernel w8_linear_invariant runs for this shape (the choice also looks at whether
+    `scales` is 16-byte aligned; None means aligned).  Host-side only."""
+    ptr = ctypes.c_void_p(scales.data_ptr() if scales is not None else 256)
+    return _lib.w8_linear_invariant_kernel(int(N), int(K), int(T_pad), ptr).decode()
 
 
 def vocab_block_logprob_workspace_bytes(t: int, V: int, block: int) -> int:

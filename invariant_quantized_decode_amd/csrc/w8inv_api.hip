@@ -63,6 +63,11 @@ int w8_linear_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_
     return launch_linear(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
 }
 
+const char* w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t* scales) {
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return "";
+    return linear_kernel_name(N, K, T_pad, scales);
+}
+
 size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) {
     if (t <= 0 || V <= 0 || block < 256 || block > 32768 || (block & (block - 1)) != 0) return 0;
     return logprob_workspace_bytes(t, V, block);

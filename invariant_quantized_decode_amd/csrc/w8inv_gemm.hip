@@ -819,48 +819,92 @@ static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, i
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 
-int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
-                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
-    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256)
-        return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, stream);
-    const dim3 grid((unsigned)((N + kRows - 1) / kRows));
-    const dim3 block(kGemmThreads);
+// The kernel a call runs: a function of (N, K, T_pad) and of the scales'
+// 16-byte alignment, never of t.  All kernels share the K plan, so the choice
+// changes no bit of the result.
+enum class LinearKernel { kTiles, kSplitLds, kSplitRegs, kNone };
+struct LinearPlan {
+    LinearKernel kind;
+    int tp16;   // T_pad / 16
+    int depth;  // ring depth of the LDS-staged split kernel
+};
+
+static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
+    const int tp16 = T_pad / 16;
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return {LinearKernel::kTiles, tp16, 0};
     // T_pad <= 32 with the strip's scales loadable as 16-byte pieces: the
     // LDS-staged variant, with the deepest ring whose LDS leaves room for them
     const int64_t s_bytes = (64 * (K / kGroup) + kLdsDmaBytes - 1) / kLdsDmaBytes * kLdsDmaBytes;
     if (T_pad <= 32 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {
-        const int tp = T_pad / 16;
-#define W8I_SPLIT_LAUNCH(D)                                                                                  \
-    if (s_bytes <= split_lds_scale_bytes(D)) {                                                               \
-        if (tp == 1)                                                                                         \
-            hipLaunchKernelGGL((gemm_w8g32_split_lds<1, D>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy); \
-        else                                                                                                 \
-            hipLaunchKernelGGL((gemm_w8g32_split_lds<2, D>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy); \
-        return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;                                          \
+        for (int D = 4; D >= 2; --D)
+            if (s_bytes <= split_lds_scale_bytes(D)) return {LinearKernel::kSplitLds, tp16, D};
     }
-        W8I_SPLIT_LAUNCH(4)
-        W8I_SPLIT_LAUNCH(3)
-        W8I_SPLIT_LAUNCH(2)
+    if (gemm_lds_bytes(K, (tp16 + 1) / 2) > kMaxGemmLds) return {LinearKernel::kNone, tp16, 0};
+    return {LinearKernel::kSplitRegs, tp16, 0};
+}
+
+const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
+    static const char* const tiles[] = {"gemm_w8g32_tiles<1>", "gemm_w8g32_tiles<2>"};
+    static const char* const split_lds[2][3] = {
+        {"gemm_w8g32_split_lds<1, 2>", "gemm_w8g32_split_lds<1, 3>", "gemm_w8g32_split_lds<1, 4>"},
+        {"gemm_w8g32_split_lds<2, 2>", "gemm_w8g32_split_lds<2, 3>", "gemm_w8g32_split_lds<2, 4>"}};
+    static const char* const regs[] = {"gemm_w8g32_fixed_width<1>", "gemm_w8g32_fixed_width<2>",
+                                       "gemm_w8g32_fixed_width<3>", "gemm_w8g32_fixed_width<4>"};
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
+    const LinearPlan p = plan_linear(N, K, T_pad, S);
+    switch (p.kind) {
+        case LinearKernel::kTiles: return tiles[p.tp16 - 1];
+        case LinearKernel::kSplitLds: return split_lds[p.tp16 - 1][p.depth - 2];
+        case LinearKernel::kSplitRegs: return regs[p.tp16 - 1];
+        default: return "";
+    }
+}
+
+int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
+                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+    const LinearPlan p = plan_linear(N, K, T_pad, S);
+    const dim3 grid((unsigned)((N + kRows - 1) / kRows));
+    const dim3 block(kGemmThreads);
+    switch (p.kind) {
+        case LinearKernel::kTiles:
+            return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, stream);
+        case LinearKernel::kSplitLds: {
+#define W8I_SPLIT_LAUNCH(TP, D)                                                                                  \
+    case TP * 8 + D:                                                                                             \
+        hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy); \
+        break;
+            switch (p.tp16 * 8 + p.depth) {
+                W8I_SPLIT_LAUNCH(1, 2)
+                W8I_SPLIT_LAUNCH(1, 3)
+                W8I_SPLIT_LAUNCH(1, 4)
+                W8I_SPLIT_LAUNCH(2, 2)
+                W8I_SPLIT_LAUNCH(2, 3)
+                W8I_SPLIT_LAUNCH(2, 4)
+                default:
+                    return W8I_ET;
+            }
 #undef W8I_SPLIT_LAUNCH
-    }
-    const int NT = (T_pad / 16 + 1) / 2;
-    const size_t lds = gemm_lds_bytes(K, NT);
-    if (lds > kMaxGemmLds) return W8I_ESHAPE;
-    switch (T_pad / 16) {
-        case 1:
-            hipLaunchKernelGGL(gemm_w8g32_fixed_width<1>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
             break;
-        case 2:
-            hipLaunchKernelGGL(gemm_w8g32_fixed_width<2>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
+        }
+        case LinearKernel::kSplitRegs: {
+            const size_t lds = gemm_lds_bytes(K, (p.tp16 + 1) / 2);
+            switch (p.tp16) {
+#define W8I_REGS_LAUNCH(TP)                                                                                      \
+    case TP:                                                                                                     \
+        hipLaunchKernelGGL(gemm_w8g32_fixed_width<TP>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy); \
+        break;
+                W8I_REGS_LAUNCH(1)
+                W8I_REGS_LAUNCH(2)
+                W8I_REGS_LAUNCH(3)
+                W8I_REGS_LAUNCH(4)
+#undef W8I_REGS_LAUNCH
+                default:
+                    return W8I_ET;
+            }
             break;
-        case 3:
-            hipLaunchKernelGGL(gemm_w8g32_fixed_width<3>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
-            break;
-        case 4:
-            hipLaunchKernelGGL(gemm_w8g32_fixed_width<4>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy);
-            break;
+        }
         default:
-            return W8I_ET;
+            return W8I_ESHAPE;
     }
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }

@@ -22,6 +22,7 @@ __host__ __device__ __forceinline__ int64_t kslice_begin(int64_t G, int i) {
 
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                   int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S);
 
 size_t logprob_workspace_bytes(int t, int64_t V, int block);
 int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,

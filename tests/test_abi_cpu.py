@@ -21,10 +21,21 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
+
+
+def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
+    """The kernel-name query is host-only; it names one kernel per (N, K, T_pad, scales alignment)."""
+    q = L.w8_linear_invariant_kernel
+    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 4>"
+    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_fixed_width<2>"   # scales not 16-byte aligned
+    assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2>"
+    assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_fixed_width<4>"
+    for bad in ((6144, 5100, 32), (0, 5120, 32), (6144, 5120, 24), (6144, 5120, 80)):
+        assert q(*bad, fake(4096)) == b""
 
 
 def test_status_strings_and_version():
