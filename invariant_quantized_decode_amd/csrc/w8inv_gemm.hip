@@ -13,8 +13,9 @@
 //    pairs of 32-element groups (kslice_begin), each summed in ascending
 //    group order in fp64, the 8 slice sums combined by a left fold.  Two
 //    kernels run this same plan and give the same bits for every row:
-//    - gemm_w8g32_fixed_width: one workgroup = 32 output rows x all K, its 8
-//      waves take the 8 slices; slice sums meet in LDS, wave 0 folds them.
+//    - gemm_w8g32_split_lds: one workgroup = 32 output rows x all K, its 8
+//      waves take the 8 slices; activations and scales are staged in LDS by
+//      direct loads; the slice sums meet in LDS and are folded there.
 //    - gemm_w8g32_tiles (large N, T_pad <= 32): persistent workgroups stream
 //      256-row tiles; each wave owns a 32-row strip and walks all of K,
 //      keeping the running slice sum and the fold in registers, while the
@@ -27,7 +28,7 @@
 //  * The fp16 group scale is applied to that fp32 group sum in fp64 (the
 //    product is exact there); the fp64 result is rounded once to bf16.
 //  * Every one of the T_pad columns goes through the matrix core for every t;
-//    columns >= t are zero registers, never loaded and never stored.
+//    columns >= t read column t - 1 (valid memory) and are never stored.
 //  * No atomics; nothing depends on t, T_pad, N or the device.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -63,25 +64,13 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q0, uint32_t q1) {
 }
 
 // ----------------------------------------------------------------------------
-// Loads.  A stage is two consecutive groups.  One load instruction covers 16
-// rows (or 16 activation columns) x 64 contiguous bytes, so every row segment
-// is read whole; the matrix-core layout (lane = row + 32 * half) is then
-// restored in registers with v_permlane16_swap, which exchanges lane bit 4
-// with the index of the register pair:
-//   weights     lane l of instruction i reads row 16 i + (l & 15),
-//               group (l >> 4) & 1 of the stage, 16-byte half l >> 5;
-//   activations lane l of instruction (gs, i) reads column 16 i + (l & 15),
-//               group gs, byte offset 32 (l >> 5) + 16 ((l >> 4) & 1).
-// After the swap, register pair slot 0 / 1 holds group 0 / 1 (weights) or
-// half 0 / 1 of the group (activations) in the layout the MFMA reads.
+// Weight loads.  A stage is two consecutive groups.  One load instruction
+// covers 16 rows x 64 contiguous bytes: lane l of instruction i reads row
+// 16 i + (l & 15), group (l >> 4) & 1 of the stage, 16-byte half l >> 5.  The
+// matrix-core layout (lane = row + 32 * half) is then restored in registers
+// with v_permlane16_swap, which exchanges lane bit 4 with the index of the
+// register pair: afterwards register slot 0 / 1 holds group 0 / 1.
 // ----------------------------------------------------------------------------
-
-// Row stride (in 16-bit scales) of the strip's scales in LDS: at least G, and
-// an odd number of dwords, so the 32 rows read in one instruction fall in 32
-// different banks.
-__host__ __device__ __forceinline__ int scale_row_stride(int64_t G) {
-    return 2 * ((int)((G + 1) / 2) | 1);
-}
 
 __device__ __forceinline__ void swap16(u32x4& a, u32x4& b) {
 #pragma unroll
@@ -92,273 +81,29 @@ __device__ __forceinline__ void swap16(u32x4& a, u32x4& b) {
     }
 }
 
-template <int NT>
-struct Stage {
-    u32x4 w[2];          // [instruction i] -> after swap16: [group of the stage]
-    u32x4 x[NT][2][2];   // [tile][group gs][instruction i] -> after swap16: [tile][gs][half h]
-};
-
-// Ring depth in stages: every load of stage k + D is issued while stage k is
-// consumed, and all loads use the same distance because the memory counter
-// retires them in issue order.
-template <int NT>
-struct Ring {
-    static constexpr int depth = NT == 1 ? 4 : 2;
-};
-
-template <int TP16>  // T_pad / 16
-__global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_fixed_width(
-    const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy) {
-    constexpr int NT = (TP16 + 1) / 2;                // 32-column tiles
-    constexpr int D = Ring<NT>::depth;
-    constexpr int kLastValues = (TP16 & 1) ? 8 : 16;  // real rows of the last tile's 16 per lane
-    // LDS: the strip's scales during the main loop, then the 7 partials the
-    // left fold consumes (the two uses are separated by a barrier)
-    extern __shared__ __align__(16) unsigned char lds[];
-    uint16_t* s_lds = reinterpret_cast<uint16_t*>(lds);
-    double* fold = reinterpret_cast<double*>(lds);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = (int)(K / kGroup);
-    const int s_stride = scale_row_stride(G);
-    const int64_t n0 = (int64_t)blockIdx.x * kRows;
-
-    const int g_begin = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave));
-    const int g_end = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave + 1));
-
-    // Buffer resources: the per-lane offsets below are fixed for the whole
-    // kernel and the stage offset is a scalar.  Rows past N read row N-1,
-    // columns past t read column t-1 (valid memory, results never stored);
-    // the descriptors' ranges also bound every access.
-    const __amdgpu_buffer_rsrc_t w_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(N * K), 0x00020000);
-    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
-    uint32_t w_off[2];     // this lane's weight piece in group 0 of the stage
-    uint32_t w_off_gs[2];  // ... in the group it carries, (lane >> 4) & 1
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t nr = n0 + 16 * i + (lane & 15);
-        w_off[i] = (uint32_t)((nr < N ? nr : N - 1) * K) + 16u * (lane >> 5);
-        w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
-    }
-    uint32_t x_off[NT][2];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int j = 32 * tt + 16 * i + (lane & 15);
-            const int jc = j < t ? j : t - 1;
-            x_off[tt][i] = (uint32_t)(jc * ldx) * 2u + 32u * (lane >> 5) + 16u * ((lane >> 4) & 1);
-        }
-    const int r = lane & 31;  // weight row of this lane after the swaps (B column, D column)
-    const int c = lane >> 5;
-
-    double acc[NT][16];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[tt][v] = 0.0;
-
-    const int len = g_end - g_begin;
-    const int full = len >> 1;  // stages with two groups of this slice
-    const int odd = len & 1;    // the row's last group when K/32 is odd (last slice only)
-    // Prefetches past the slice's last full stage are clamped to it: they
-    // re-read cached lines instead of the next slice's data.
-    const int last_full = g_begin + 2 * (full > 0 ? full - 1 : 0);
-
-    // stage starting at group g: both groups lie inside the slice
-    auto load_stage = [&](int g, Stage<NT>& st) {
-        const int gc = min(g, last_full);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off_gs[i], gc * kGroup, 0));
-#pragma unroll
-        for (int gs = 0; gs < 2; ++gs)
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    st.x[tt][gs][i] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, x_off[tt][i], (gc + gs) * (2 * kGroup), 0));
-    };
-    // the single group g in position 0 (position 1 repeats it, never consumed)
-    auto load_single = [&](int g, Stage<NT>& st) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[i], g * kGroup, 0));
-#pragma unroll
-        for (int gs = 0; gs < 2; ++gs)
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    st.x[tt][gs][i] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, x_off[tt][i], g * (2 * kGroup), 0));
-    };
-    auto arrange = [&](Stage<NT>& st) {
-        swap16(st.w[0], st.w[1]);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-            for (int gs = 0; gs < 2; ++gs) swap16(st.x[tt][gs][0], st.x[tt][gs][1]);
-    };
-    // one group's products, summed by the matrix core from zero
-    auto group_mfma = [&](const Stage<NT>& st, int gs, f32x16 (&d)[NT]) {
-        const bf16x8 b_lo = dequant8(st.w[gs].x, st.w[gs].y);
-        const bf16x8 b_hi = dequant8(st.w[gs].z, st.w[gs].w);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const f32x16 zero = {};
-            d[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.x[tt][gs][0]), b_lo,
-                                                            zero, 0, 0, 0);
-            d[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.x[tt][gs][1]), b_hi,
-                                                            d[tt], 0, 0, 0);
-        }
-    };
-    // acc += s * D_g in fp64 (the product is exact there), groups ascending
-    auto step = [&](const Stage<NT>& st, int gs, int g) {
-        f32x16 d[NT];
-        group_mfma(st, gs, d);
-        const double sc = (double)(float)__builtin_bit_cast(_Float16, s_lds[r * s_stride + g]);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int nv = (tt == NT - 1) ? kLastValues : 16;
-#pragma unroll
-            for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc, (double)d[tt][v], acc[tt][v]);
-        }
-    };
-
-    Stage<NT> ring[D];
-    if (full > 0) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u]);
-    }
-    // (issued after the first stages, so both latencies overlap)
-    // The strip's scales -> LDS: 16 threads per row, each taking every 16th
-    // group, 8 loads in flight at a time (rows past N read zeros from the
-    // descriptor's range check; they are never stored).
-    {
-        const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(N * G * 2), 0x00020000);
-        const int rr = threadIdx.x >> 4, c0 = threadIdx.x & 15;
-        const uint32_t row_off = (uint32_t)((n0 + rr) * G) * 2u;
-        for (int cb = c0; cb < G; cb += 16 * 8) {
-            uint16_t v[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int col = cb + 16 * q;
-                v[q] = col < G ? __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, row_off + 2u * col, 0, 0) : 0;
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int col = cb + 16 * q;
-                if (col < G) s_lds[rr * s_stride + col] = v[q];
-            }
-        }
-    }
-    __syncthreads();
-
-    if (full > 0) {
-        int g = g_begin;
-        const int nblocks = full / D;
-        for (int blk = 0; blk < nblocks; ++blk) {
-#pragma unroll
-            for (int u = 0; u < D; ++u) {
-                arrange(ring[u]);
-                step(ring[u], 0, g);
-                step(ring[u], 1, g + 1);
-                // keep the refill after this stage's compute: hoisting it
-                // would need a second set of stage registers
-                __builtin_amdgcn_sched_barrier(0);
-                load_stage(g + 2 * D, ring[u]);
-                __builtin_amdgcn_sched_barrier(0);
-                g += 2;
-            }
-        }
-        // the remaining full stages (fewer than D) were loaded already
-        switch (full - nblocks * D) {
-#define W8I_TAIL(R)                                     \
-    case R:                                             \
-        _Pragma("unroll") for (int u = 0; u < R; ++u) { \
-            arrange(ring[u]);                           \
-            step(ring[u], 0, g);                        \
-            step(ring[u], 1, g + 1);                    \
-            g += 2;                                     \
-        }                                               \
-        break;
-            W8I_TAIL(1)
-            W8I_TAIL(2)
-            W8I_TAIL(3)
-            W8I_TAIL(4)
-            W8I_TAIL(5)
-#undef W8I_TAIL
-            default:
-                break;
-        }
-    }
-    if (odd) {
-        Stage<NT> st;
-        load_single(g_end - 1, st);
-        arrange(st);
-        step(st, 0, g_end - 1);
-    }
-
-    // left fold of the 8 slice sums: ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7
-    __syncthreads();  // the scales' LDS becomes the fold buffer
-    constexpr int kVals = NT * 16;
-    if (wave > 0) {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-            for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v)
-                fold[((wave - 1) * kVals + tt * 16 + v) * 64 + lane] = acc[tt][v];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int w = 1; w < kKSlices; ++w)
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v)
-                    acc[tt][v] = acc[tt][v] + fold[((w - 1) * kVals + tt * 16 + v) * 64 + lane];
-        const int64_t n = n0 + r;
-        if (n < N) {
-            // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
-            // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns) of the tile
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
-                    const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
-                    if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(acc[tt][v]);
-                }
-        }
-    }
-}
-
 // ----------------------------------------------------------------------------
-// T_pad <= 32: the same split-K schedule with the activations and the scales
-// staged in LDS by direct loads (buffer_load ... lds).  Every wave re-reads
-// its slice's activations from L2, and what that costs is the number of cache
-// lines touched, not the bytes: each direct load covers 8 columns x 128 bytes
-// (whole lines) and lands in a per-wave LDS ring of depth D, from which the
+// Split-K: one workgroup = 32 output rows x all K, its 8 waves take the 8
+// K-slices, the slice sums meet in LDS.  Activations and scales are staged in
+// LDS by direct loads (buffer_load ... lds).  Every wave re-reads its slice's
+// activations from L2, and what that costs is the number of cache lines
+// touched, not the bytes: each direct load covers 8 columns x 128 bytes (whole
+// lines) and lands in a per-wave LDS ring of depth D, from which the
 // matrix-core operands are read.  The strip's scales (rows n0 .. n0+31) are
 // one contiguous block of 64 G bytes and are copied to LDS before the main
-// loop.  The arithmetic, and so every bit, is that of the kernel above.
+// loop when they fit beside the ring; otherwise each stage loads its scales
+// with the weights.
 // ----------------------------------------------------------------------------
 #define W8I_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kXStageBytes = 32 * 128;                    // 32 columns x one stage of bf16
-constexpr int kXSlotBytes = kKSlices * kXStageBytes;      // one ring slot of all 8 waves
-constexpr int kLdsDmaBytes = 1024;                        // bytes of one wave-wide 16-byte direct load
+constexpr int kXTileBytes = 32 * 128;  // 32 columns x one stage of bf16
+constexpr int kLdsDmaBytes = 1024;     // bytes of one wave-wide 16-byte direct load
+
+// one ring slot (the stage of all 8 waves) for NT 32-column tiles
+__host__ __device__ constexpr int split_lds_slot_bytes(int NT) { return kKSlices * NT * kXTileBytes; }
 
 // LDS capacity left for the scales when the ring has D slots
-__host__ __device__ constexpr int split_lds_scale_bytes(int D) {
-    return (int)kMaxGemmLds - D * kXSlotBytes - (4 - D) * 16;
+__host__ __device__ constexpr int split_lds_scale_bytes(int NT, int D) {
+    return (int)kMaxGemmLds - D * split_lds_slot_bytes(NT) - (4 - D) * 16;
 }
 
 // Byte offset of 16-byte piece p (0..7) of column a inside a wave's stage:
@@ -368,23 +113,34 @@ __host__ __device__ constexpr int split_lds_scale_bytes(int D) {
 // (l & 7) ^ ((l >> 3) & 7).
 __device__ __forceinline__ uint32_t xs_off(int a, int p) { return (uint32_t)(a * 128 + 16 * (p ^ (a & 7))); }
 
-// s_waitcnt that waits until at most n vector-memory operations are pending
-#define W8I_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+// s_waitcnt that waits until at most N vector-memory operations are pending
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-template <int TP16, int D>  // TP16 = T_pad / 16 (1 or 2), D = ring depth in stages (2..4)
+// LS: the strip's scales are copied to LDS (when they fit beside the ring);
+// otherwise every stage loads its two scales per row with the weights.
+template <int TP16, int D, bool LS>  // TP16 = T_pad / 16 (1..4), D = ring depth in stages (2..4)
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy) {
-    static_assert(TP16 == 1 || TP16 == 2, "one 32-column tile");
+    static_assert(TP16 >= 1 && TP16 <= 4, "T_pad 16..64");
     static_assert(D >= 2 && D <= 4, "ring depth");
-    constexpr int kLastValues = TP16 == 1 ? 8 : 16;
-    constexpr int kScaleBytes = split_lds_scale_bytes(D);
-    constexpr int kLoadsPerStage = 2 + 4;  // weight loads + direct activation loads
+    constexpr int NT = (TP16 + 1) / 2;                // 32-column tiles
+    constexpr int kLastValues = (TP16 & 1) ? 8 : 16;  // real rows of the last tile's 16 per lane
+    constexpr int kStageBytes = NT * kXTileBytes;     // one wave's activation stage
+    constexpr int kSlotBytes = split_lds_slot_bytes(NT);
+    constexpr int kScaleBytes = LS ? split_lds_scale_bytes(NT, D) : 16;
+    constexpr int kXLoads = 4 * NT;                   // direct loads of 8 columns x 128 bytes per stage
+    constexpr int kLoadsPerStage = 2 + kXLoads + (LS ? 0 : 2);  // weights + activations (+ scales)
+    static_assert(kScaleBytes > 0, "LDS");
     // one array per ring slot, so the compiler can wait for each slot's loads alone
-    __shared__ __align__(16) unsigned char xr0[kXSlotBytes];
-    __shared__ __align__(16) unsigned char xr1[kXSlotBytes];
-    __shared__ __align__(16) unsigned char xr2[D > 2 ? kXSlotBytes : 16];
-    __shared__ __align__(16) unsigned char xr3[D > 3 ? kXSlotBytes : 16];
+    __shared__ __align__(16) unsigned char xr0[kSlotBytes];
+    __shared__ __align__(16) unsigned char xr1[kSlotBytes];
+    __shared__ __align__(16) unsigned char xr2[D > 2 ? kSlotBytes : 16];
+    __shared__ __align__(16) unsigned char xr3[D > 3 ? kSlotBytes : 16];
     __shared__ __align__(16) unsigned char s_raw[kScaleBytes];
     const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(s_raw);
 
@@ -410,7 +166,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 
     // the strip's scales -> LDS, issued first so the wait below can leave the
     // activation ring in flight
-    const int s_loads = (64 * G + kLdsDmaBytes - 1) / kLdsDmaBytes;
+    const int s_loads = LS ? (64 * G + kLdsDmaBytes - 1) / kLdsDmaBytes : 0;
     for (int k = wave; k < s_loads; k += kKSlices)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, W8I_LDS(s_raw + k * kLdsDmaBytes), 16, 16u * lane,
                                                  (uint32_t)(n0 * G * 2) + (uint32_t)(k * kLdsDmaBytes), 0, 0);
@@ -423,26 +179,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         w_off[i] = (uint32_t)((nr < N ? nr : N - 1) * K) + 16u * (lane >> 5);
         w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
     }
-    uint32_t xd_off[4];  // direct load i of a stage: columns 8 i .. 8 i + 7
+    // direct load i of a stage: columns 8 i .. 8 i + 7 (sized for two tiles: an
+    // array whose size depends on the template arguments, captured by the
+    // lambdas below, made the host pass drop the kernel stubs)
+    uint32_t xd_off[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kXLoads; ++i) {
         const int a = 8 * i + (lane >> 3);
         const int jc = a < t ? a : t - 1;
         xd_off[i] = (uint32_t)(jc * ldx) * 2u + 16u * ((lane & 7) ^ ((lane >> 3) & 7));
     }
     const int r = lane & 31;  // weight row of this lane after the swaps (B column, D column)
     const int c = lane >> 5;
-    // matrix-core A operand: lane (r, c) takes K [16 c, 16 c + 16) of group gs
-    // of column r = pieces 4 gs + 2 c (first MFMA) and 4 gs + 2 c + 1 (second)
-    uint32_t xa_off[2][2];
+    // matrix-core A operand of tile tt: lane (r, c) takes K [16 c, 16 c + 16)
+    // of group gs of column 32 tt + r = pieces 4 gs + 2 c (first MFMA) and
+    // 4 gs + 2 c + 1 (second)
+    uint32_t xa_off[NT][2][2];
 #pragma unroll
-    for (int gs = 0; gs < 2; ++gs)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) xa_off[gs][h] = (uint32_t)(wave * kXStageBytes) + xs_off(r, 4 * gs + 2 * c + h);
+        for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                xa_off[tt][gs][h] = (uint32_t)(wave * kStageBytes) + xs_off(32 * tt + r, 4 * gs + 2 * c + h);
 
-    double acc[16];
+    double acc[NT][16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0;
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[tt][v] = 0.0;
 
     const int len = g_end - g_begin;
     const int full = len >> 1;
@@ -455,52 +220,70 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t x_none =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_none =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(S), (short)0, 0, 0x00020000);
+    // this lane's row of scales (per-stage scale loads)
+    const uint32_t s_row_off = (uint32_t)((n0 + r < N ? n0 + r : N - 1) * G) * 2u;
 
     auto slot = [&](int u) -> unsigned char* { return u == 0 ? xr0 : u == 1 ? xr1 : u == 2 ? xr2 : xr3; };
     // stage starting at group g; `single` loads group g alone in position 0
     // (the odd last group)
-    auto load_stage = [&](int g, u32x4 (&w)[2], unsigned char* xs, bool single) {
+    auto load_stage = [&](int g, u32x4 (&w)[2], uint16_t (&sc)[2], unsigned char* xs, bool single) {
         const bool live = single || g <= last_full;
         const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
         const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
+        if constexpr (!LS) {
+            const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
+            sc[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * g, 0, 0);
+            sc[1] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * (single ? g : g + 1), 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, W8I_LDS(xs + wave * kXStageBytes + i * kLdsDmaBytes), 16,
+        for (int i = 0; i < kXLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, W8I_LDS(xs + wave * kStageBytes + i * kLdsDmaBytes), 16,
                                                      xd_off[i], g * (2 * kGroup), 0, 0);
     };
     // group gs of the stage (weights already swapped), acc += s * D_g in fp64
-    auto step = [&](const u32x4 (&w)[2], const unsigned char* xs, int gs, int g) {
+    auto step = [&](const u32x4 (&w)[2], const uint16_t (&ss)[2], const unsigned char* xs, int gs, int g) {
         const bf16x8 b_lo = dequant8(w[gs].x, w[gs].y);
         const bf16x8 b_hi = dequant8(w[gs].z, w[gs].w);
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + xa_off[gs][0]);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + xa_off[gs][1]);
-        const f32x16 zero = {};
-        f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo, zero, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
-        const double sc = (double)(float)__builtin_bit_cast(_Float16, s_lds[r * G + g]);
+        const uint16_t s16 = LS ? s_lds[r * G + g] : ss[gs];
+        const double sc = (double)(float)__builtin_bit_cast(_Float16, s16);
 #pragma unroll
-        for (int v = 0; v < kLastValues; ++v) acc[v] = __builtin_fma(sc, (double)d[v], acc[v]);
+        for (int tt = 0; tt < NT; ++tt) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + xa_off[tt][gs][0]);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + xa_off[tt][gs][1]);
+            const f32x16 zero = {};
+            f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo, zero, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
+            const int nv = (tt == NT - 1) ? kLastValues : 16;
+#pragma unroll
+            for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc, (double)d[v], acc[tt][v]);
+        }
     };
 
     u32x4 ring[D][2];
+    uint16_t sring[D][2];
     if (full > 0) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u], slot(u), false);
-        W8I_WAIT_VM(kLoadsPerStage * D);  // this wave's scale loads have landed
-    } else {
-        W8I_WAIT_VM(0);
+        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u], sring[u], slot(u), false);
     }
-    // Every wave's scale loads have landed.  A plain barrier: __syncthreads()
-    // would also wait for the activation ring's loads (its release fence
-    // covers all pending LDS writes).  The signal fences keep the compiler
-    // from moving LDS accesses across it.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if constexpr (LS) {
+        if (full > 0)
+            wait_vm<kLoadsPerStage * D>();  // this wave's scale loads have landed
+        else
+            wait_vm<0>();
+        // Every wave's scale loads have landed.  A plain barrier: __syncthreads()
+        // would also wait for the activation ring's loads (its release fence
+        // covers all pending LDS writes).  The signal fences keep the compiler
+        // from moving LDS accesses across it.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
 
     int g = g_begin;
     if (full > 0) {
@@ -511,12 +294,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         for (int blk = 0; blk < nblocks; ++blk) {
 #pragma unroll
             for (int u = 0; u < D; ++u) {
-                W8I_WAIT_VM(kLoadsPerStage * (D - 1));
+                wait_vm<kLoadsPerStage * (D - 1)>();
                 swap16(ring[u][0], ring[u][1]);
-                step(ring[u], slot(u), 0, g);
-                step(ring[u], slot(u), 1, g + 1);
+                step(ring[u], sring[u], slot(u), 0, g);
+                step(ring[u], sring[u], slot(u), 1, g + 1);
                 __builtin_amdgcn_sched_barrier(0);
-                load_stage(g + 2 * D, ring[u], slot(u), false);
+                load_stage(g + 2 * D, ring[u], sring[u], slot(u), false);
                 __builtin_amdgcn_sched_barrier(0);
                 g += 2;
             }
@@ -526,10 +309,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         auto tail_stage = [&](auto U) {
             constexpr int u = decltype(U)::value;
             if constexpr (u <= D - 2) {  // a tail has at most D - 1 stages
-                W8I_WAIT_VM(kLoadsPerStage * (D - 1 - u));
+                wait_vm<kLoadsPerStage * (D - 1 - u)>();
                 swap16(ring[u][0], ring[u][1]);
-                step(ring[u], slot(u), 0, g);
-                step(ring[u], slot(u), 1, g + 1);
+                step(ring[u], sring[u], slot(u), 0, g);
+                step(ring[u], sring[u], slot(u), 1, g + 1);
                 g += 2;
             }
         };
@@ -547,35 +330,43 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         // the row's last group (slice 7 when K/32 is odd); the ring is drained
         // and slot 0's region of this wave is free
         u32x4 w1[2];
-        load_stage(g_end - 1, w1, xr0, true);
-        W8I_WAIT_VM(0);
+        uint16_t s1[2];
+        load_stage(g_end - 1, w1, s1, xr0, true);
+        wait_vm<0>();
         swap16(w1[0], w1[1]);
-        step(w1, xr0, 0, g_end - 1);
+        step(w1, s1, xr0, 0, g_end - 1);
     }
 
     // Left fold of the 8 slice sums, ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7,
-    // shared by the waves: every slice sum goes to ring slots 0 and 1 (8 KB
-    // per wave), then wave w folds and stores values v = w, w + 8 of every
-    // lane.  The barrier's fence also waits for the prefetches past the slice
-    // ends, which still write into the ring.
+    // shared by the waves: every slice sum goes to ring slots 0 and 1
+    // (NT * 8 KB per wave, four waves per slot), then wave w folds and stores
+    // values V = w, w + 8, ... (V = 16 tt + v) of every lane.  The barrier's
+    // fence also waits for the prefetches past the slice ends, which still
+    // write into the ring.
     __syncthreads();
-    auto part_of = [&](int w) { return reinterpret_cast<double*>((w < 4 ? xr0 : xr1) + (w & 3) * (16 * 64 * 8)); };
+    auto part_of = [&](int w) {
+        return reinterpret_cast<double*>((w < 4 ? xr0 : xr1) + (w & 3) * (NT * 16 * 64 * 8));
+    };
     {
         double* f = part_of(wave);
 #pragma unroll
-        for (int v = 0; v < kLastValues; ++v) f[v * 64 + lane] = acc[v];
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) f[(tt * 16 + v) * 64 + lane] = acc[tt][v];
     }
     __syncthreads();
     const int64_t n = n0 + r;
 #pragma unroll
-    for (int k = 0; k < kLastValues / kKSlices; ++k) {
-        const int v = wave + kKSlices * k;
-        double sum = part_of(0)[v * 64 + lane];
+    for (int k = 0; k < 2 * NT; ++k) {
+        const int V = wave + kKSlices * k;
+        const int tt = V >> 4, v = V & 15;
+        if (v >= ((tt == NT - 1) ? kLastValues : 16)) continue;
+        double sum = part_of(0)[V * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kKSlices; ++w) sum = sum + part_of(w)[v * 64 + lane];
+        for (int w = 1; w < kKSlices; ++w) sum = sum + part_of(w)[V * 64 + lane];
         // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
-        // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns)
-        const int j = 8 * (v >> 2) + 4 * c + (v & 3);
+        // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns) of tile tt
+        const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
         if (n < N && j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(sum);
     }
 }
@@ -786,14 +577,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     }
 }
 
-// dynamic LDS of one workgroup: max(scales, fold partials)
-static size_t gemm_lds_bytes(int64_t K, int NT) {
-    const int64_t G = K / kGroup;
-    const size_t scales = (size_t)kRows * scale_row_stride(G) * 2;
-    const size_t partials = (size_t)(kKSlices - 1) * NT * 16 * 64 * sizeof(double);
-    return scales > partials ? scales : partials;
-}
-
 // Tiles of the persistent kernel; it is used when there are enough of them
 // to keep every CU busy for several tiles.
 static int tile_count(int64_t N) { return (int)((N + kTileStrips * kRows - 1) / (kTileStrips * kRows)); }
@@ -822,40 +605,46 @@ static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, i
 // The kernel a call runs: a function of (N, K, T_pad) and of the scales'
 // 16-byte alignment, never of t.  All kernels share the K plan, so the choice
 // changes no bit of the result.
-enum class LinearKernel { kTiles, kSplitLds, kSplitRegs, kNone };
+enum class LinearKernel { kTiles, kSplitLds };
 struct LinearPlan {
     LinearKernel kind;
-    int tp16;   // T_pad / 16
-    int depth;  // ring depth of the LDS-staged split kernel
+    int tp16;         // T_pad / 16
+    int depth;        // ring depth of the LDS-staged split kernel
+    bool lds_scales;  // ... and whether it copies the scales to LDS
 };
 
 static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
     const int tp16 = T_pad / 16;
-    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return {LinearKernel::kTiles, tp16, 0};
-    // T_pad <= 32 with the strip's scales loadable as 16-byte pieces: the
-    // LDS-staged variant, with the deepest ring whose LDS leaves room for them
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return {LinearKernel::kTiles, tp16, 0, false};
+    // the LDS-staged variant: with the deepest ring (4..2 stages for one
+    // 32-column tile, 2 for two) whose LDS leaves room for the strip's scales
+    // when they can be copied as 16-byte pieces (scales 16-byte aligned);
+    // otherwise with the deepest ring and the scales loaded per stage
     const int64_t s_bytes = (64 * (K / kGroup) + kLdsDmaBytes - 1) / kLdsDmaBytes * kLdsDmaBytes;
-    if (T_pad <= 32 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {
-        for (int D = 4; D >= 2; --D)
-            if (s_bytes <= split_lds_scale_bytes(D)) return {LinearKernel::kSplitLds, tp16, D};
+    const int nt = (tp16 + 1) / 2;
+    const int dmax = nt == 1 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(S) & 15) == 0) {
+        for (int D = dmax; D >= 2; --D)
+            if (s_bytes <= split_lds_scale_bytes(nt, D)) return {LinearKernel::kSplitLds, tp16, D, true};
     }
-    if (gemm_lds_bytes(K, (tp16 + 1) / 2) > kMaxGemmLds) return {LinearKernel::kNone, tp16, 0};
-    return {LinearKernel::kSplitRegs, tp16, 0};
+    return {LinearKernel::kSplitLds, tp16, dmax, false};
 }
 
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     static const char* const tiles[] = {"gemm_w8g32_tiles<1>", "gemm_w8g32_tiles<2>"};
-    static const char* const split_lds[2][3] = {
-        {"gemm_w8g32_split_lds<1, 2>", "gemm_w8g32_split_lds<1, 3>", "gemm_w8g32_split_lds<1, 4>"},
-        {"gemm_w8g32_split_lds<2, 2>", "gemm_w8g32_split_lds<2, 3>", "gemm_w8g32_split_lds<2, 4>"}};
-    static const char* const regs[] = {"gemm_w8g32_fixed_width<1>", "gemm_w8g32_fixed_width<2>",
-                                       "gemm_w8g32_fixed_width<3>", "gemm_w8g32_fixed_width<4>"};
+    static const char* const split_lds[4][3] = {
+        {"gemm_w8g32_split_lds<1, 2, true>", "gemm_w8g32_split_lds<1, 3, true>", "gemm_w8g32_split_lds<1, 4, true>"},
+        {"gemm_w8g32_split_lds<2, 2, true>", "gemm_w8g32_split_lds<2, 3, true>", "gemm_w8g32_split_lds<2, 4, true>"},
+        {"gemm_w8g32_split_lds<3, 2, true>", "", ""},
+        {"gemm_w8g32_split_lds<4, 2, true>", "", ""}};
+    static const char* const split_lds_gs[4] = {"gemm_w8g32_split_lds<1, 4, false>", "gemm_w8g32_split_lds<2, 4, false>",
+                                                "gemm_w8g32_split_lds<3, 2, false>", "gemm_w8g32_split_lds<4, 2, false>"};
     if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
     const LinearPlan p = plan_linear(N, K, T_pad, S);
     switch (p.kind) {
         case LinearKernel::kTiles: return tiles[p.tp16 - 1];
-        case LinearKernel::kSplitLds: return split_lds[p.tp16 - 1][p.depth - 2];
-        case LinearKernel::kSplitRegs: return regs[p.tp16 - 1];
+        case LinearKernel::kSplitLds:
+            return p.lds_scales ? split_lds[p.tp16 - 1][p.depth - 2] : split_lds_gs[p.tp16 - 1];
         default: return "";
     }
 }
@@ -869,38 +658,28 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
         case LinearKernel::kTiles:
             return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, stream);
         case LinearKernel::kSplitLds: {
-#define W8I_SPLIT_LAUNCH(TP, D)                                                                                  \
-    case TP * 8 + D:                                                                                             \
-        hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy); \
+#define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                  \
+    case TP * 16 + D * 2 + LS:                                                                       \
+        hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D, LS>), grid, block, 0, stream, W, S, X, Y, N, K, t, \
+                           ldx, ldy);                                                                \
         break;
-            switch (p.tp16 * 8 + p.depth) {
-                W8I_SPLIT_LAUNCH(1, 2)
-                W8I_SPLIT_LAUNCH(1, 3)
-                W8I_SPLIT_LAUNCH(1, 4)
-                W8I_SPLIT_LAUNCH(2, 2)
-                W8I_SPLIT_LAUNCH(2, 3)
-                W8I_SPLIT_LAUNCH(2, 4)
+            switch (p.tp16 * 16 + p.depth * 2 + (p.lds_scales ? 1 : 0)) {
+                W8I_SPLIT_LAUNCH(1, 2, true)
+                W8I_SPLIT_LAUNCH(1, 3, true)
+                W8I_SPLIT_LAUNCH(1, 4, true)
+                W8I_SPLIT_LAUNCH(2, 2, true)
+                W8I_SPLIT_LAUNCH(2, 3, true)
+                W8I_SPLIT_LAUNCH(2, 4, true)
+                W8I_SPLIT_LAUNCH(3, 2, true)
+                W8I_SPLIT_LAUNCH(4, 2, true)
+                W8I_SPLIT_LAUNCH(1, 4, false)
+                W8I_SPLIT_LAUNCH(2, 4, false)
+                W8I_SPLIT_LAUNCH(3, 2, false)
+                W8I_SPLIT_LAUNCH(4, 2, false)
                 default:
                     return W8I_ET;
             }
 #undef W8I_SPLIT_LAUNCH
-            break;
-        }
-        case LinearKernel::kSplitRegs: {
-            const size_t lds = gemm_lds_bytes(K, (p.tp16 + 1) / 2);
-            switch (p.tp16) {
-#define W8I_REGS_LAUNCH(TP)                                                                                      \
-    case TP:                                                                                                     \
-        hipLaunchKernelGGL(gemm_w8g32_fixed_width<TP>, grid, block, lds, stream, W, S, X, Y, N, K, t, ldx, ldy); \
-        break;
-                W8I_REGS_LAUNCH(1)
-                W8I_REGS_LAUNCH(2)
-                W8I_REGS_LAUNCH(3)
-                W8I_REGS_LAUNCH(4)
-#undef W8I_REGS_LAUNCH
-                default:
-                    return W8I_ET;
-            }
             break;
         }
         default:

@@ -188,11 +188,14 @@ def test_t_pad_and_row_slice_independence():
 
 
 # --------------------------------- the LDS-staged split-K variants (T_pad <= 32)
-STAGING = [  # N, K, t, T_pad: LDS ring depth 4 / 3 / 2 by the strip's scale bytes, then the register path
+STAGING = [  # N, K, t, T_pad: LDS ring depth 4 / 3 / 2 by the strip's scale bytes, then per-stage scales
     (257, 1056, 32, 32),   # K/32 = 33 (odd), depth 4
     (40, 17408, 5, 32),    # K/32 = 544, depth 3
     (24, 36896, 3, 16),    # K/32 = 1153 (odd), depth 2
-    (16, 64000, 16, 16),   # K/32 = 2000: scales too large for the ring variants
+    (16, 64000, 16, 16),   # K/32 = 2000: scales too large for LDS, loaded per stage
+    (70, 15872, 48, 48),   # two column tiles, depth 2, K/32 = 496 (the largest that fits)
+    (40, 16000, 64, 64),   # two column tiles, K/32 = 500 > 496: scales loaded per stage
+    (33, 16032, 64, 64),   # the same with K/32 = 501 (odd)
 ]
 
 
@@ -207,10 +210,10 @@ def test_staging_variants_match_oracle_and_row_slices(N, K, t, T_pad):
     assert np.array_equal(part, y[:, 3:]), "row slice differs"
 
 
-@pytest.mark.parametrize("T_pad", [16, 32])
+@pytest.mark.parametrize("T_pad", [16, 32, 48, 64])
 def test_unaligned_scales_give_the_same_bits(T_pad):
-    """Scales that are not 16-byte aligned cannot be copied to LDS in 16-byte pieces and take
-    the register-staged kernel; the arithmetic, and so every bit, is the same."""
+    """Scales that are not 16-byte aligned cannot be copied to LDS in 16-byte pieces and are
+    loaded per stage instead; the arithmetic, and so every bit, is the same."""
     N, K = 300, 5120
     q, s, x = synth.small_linear(77 + T_pad, N, K, T_pad, 0.0)
     Wd, Sd, Xd = i8(q), f16(s), bf16(x)
