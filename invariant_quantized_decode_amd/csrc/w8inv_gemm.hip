@@ -616,13 +616,15 @@ struct LinearPlan {
 static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
     const int tp16 = T_pad / 16;
     if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return {LinearKernel::kTiles, tp16, 0, false};
-    // the LDS-staged variant: with the deepest ring (4..2 stages for one
+    // the LDS-staged variant: with the deepest ring (3 or 2 stages for one
     // 32-column tile, 2 for two) whose LDS leaves room for the strip's scales
     // when they can be copied as 16-byte pieces (scales 16-byte aligned);
-    // otherwise with the deepest ring and the scales loaded per stage
+    // otherwise with the deepest ring and the scales loaded per stage.  (A
+    // depth of 3 measured faster than 4 at T_pad: more loads in flight only
+    // queue longer.)
     const int64_t s_bytes = (64 * (K / kGroup) + kLdsDmaBytes - 1) / kLdsDmaBytes * kLdsDmaBytes;
     const int nt = (tp16 + 1) / 2;
-    const int dmax = nt == 1 ? 4 : 2;
+    const int dmax = nt == 1 ? 3 : 2;
     if ((reinterpret_cast<uintptr_t>(S) & 15) == 0) {
         for (int D = dmax; D >= 2; --D)
             if (s_bytes <= split_lds_scale_bytes(nt, D)) return {LinearKernel::kSplitLds, tp16, D, true};
@@ -633,11 +635,11 @@ static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     static const char* const tiles[] = {"gemm_w8g32_tiles<1>", "gemm_w8g32_tiles<2>"};
     static const char* const split_lds[4][3] = {
-        {"gemm_w8g32_split_lds<1, 2, true>", "gemm_w8g32_split_lds<1, 3, true>", "gemm_w8g32_split_lds<1, 4, true>"},
-        {"gemm_w8g32_split_lds<2, 2, true>", "gemm_w8g32_split_lds<2, 3, true>", "gemm_w8g32_split_lds<2, 4, true>"},
+        {"gemm_w8g32_split_lds<1, 2, true>", "gemm_w8g32_split_lds<1, 3, true>", ""},
+        {"gemm_w8g32_split_lds<2, 2, true>", "gemm_w8g32_split_lds<2, 3, true>", ""},
         {"gemm_w8g32_split_lds<3, 2, true>", "", ""},
         {"gemm_w8g32_split_lds<4, 2, true>", "", ""}};
-    static const char* const split_lds_gs[4] = {"gemm_w8g32_split_lds<1, 4, false>", "gemm_w8g32_split_lds<2, 4, false>",
+    static const char* const split_lds_gs[4] = {"gemm_w8g32_split_lds<1, 3, false>", "gemm_w8g32_split_lds<2, 3, false>",
                                                 "gemm_w8g32_split_lds<3, 2, false>", "gemm_w8g32_split_lds<4, 2, false>"};
     if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
     const LinearPlan p = plan_linear(N, K, T_pad, S);
@@ -666,14 +668,12 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
             switch (p.tp16 * 16 + p.depth * 2 + (p.lds_scales ? 1 : 0)) {
                 W8I_SPLIT_LAUNCH(1, 2, true)
                 W8I_SPLIT_LAUNCH(1, 3, true)
-                W8I_SPLIT_LAUNCH(1, 4, true)
                 W8I_SPLIT_LAUNCH(2, 2, true)
                 W8I_SPLIT_LAUNCH(2, 3, true)
-                W8I_SPLIT_LAUNCH(2, 4, true)
                 W8I_SPLIT_LAUNCH(3, 2, true)
                 W8I_SPLIT_LAUNCH(4, 2, true)
-                W8I_SPLIT_LAUNCH(1, 4, false)
-                W8I_SPLIT_LAUNCH(2, 4, false)
+                W8I_SPLIT_LAUNCH(1, 3, false)
+                W8I_SPLIT_LAUNCH(2, 3, false)
                 W8I_SPLIT_LAUNCH(3, 2, false)
                 W8I_SPLIT_LAUNCH(4, 2, false)
                 default:

@@ -30,8 +30,8 @@ def test_every_declared_symbol_is_exported():
 def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
     """The kernel-name query is host-only; it names one kernel per (N, K, T_pad, scales alignment)."""
     q = L.w8_linear_invariant_kernel
-    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 4, true>"
-    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 4, false>"  # scales not 16-byte aligned
+    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true>"
+    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false>"  # scales not 16-byte aligned
     assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2>"
     assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true>"
     assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false>"  # scales too large for LDS

@@ -188,8 +188,8 @@ def test_t_pad_and_row_slice_independence():
 
 
 # --------------------------------- the LDS-staged split-K variants (T_pad <= 32)
-STAGING = [  # N, K, t, T_pad: LDS ring depth 4 / 3 / 2 by the strip's scale bytes, then per-stage scales
-    (257, 1056, 32, 32),   # K/32 = 33 (odd), depth 4
+STAGING = [  # N, K, t, T_pad: LDS ring depth 3 / 2 by the strip's scale bytes, then per-stage scales
+    (257, 1056, 32, 32),   # K/32 = 33 (odd), depth 3
     (40, 17408, 5, 32),    # K/32 = 544, depth 3
     (24, 36896, 3, 16),    # K/32 = 1153 (odd), depth 2
     (16, 64000, 16, 16),   # K/32 = 2000: scales too large for LDS, loaded per stage
