@@ -375,40 +375,46 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 // Large N: persistent tiles.  One workgroup per CU streams tiles of 8 strips
 // (256 rows); wave w owns strip w of the tile and walks all of K, keeping the
 // current slice's sum and the left fold of the finished slices in registers,
-// so every output gets exactly the bits of the split-K kernel above.  The
-// activation stage (2 groups x 32 columns per tile) is loaded once per
-// workgroup into a double-buffered LDS ring and read by all 8 waves.  Weight
-// and scale loads run D stages ahead across tile boundaries.
+// so every output gets exactly the bits of the split-K kernel above.
+//
+// Work goes in blocks of 4 stages (8 groups); a tile is padded to whole
+// blocks with phantom stages, whose loads use zero-range descriptors (no
+// memory traffic) and whose compute is skipped.  Per block:
+//  * the activations of the next block (32 columns x 8 groups) are copied to
+//    a double-buffered LDS ring by direct loads, 1/8 by each wave, and one
+//    barrier publishes them -- one barrier per block, not per stage;
+//  * with SC (K/32 % 8 == 0 and 16-byte aligned scales) each lane loads its
+//    row's 8 scales of the next block with one 16-byte load; otherwise every
+//    stage loads its two scales per row (two 2-byte loads per lane);
+//  * weights run one block (4 stages) ahead in a register ring.
+// The loads are issued in a fixed order, so every wait is a constant count.
 // ----------------------------------------------------------------------------
 constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
+constexpr int kBlockStages = 4;        // stages per block
 
-template <int NT>
-struct TileRing {
-    static constexpr int depth = NT == 1 ? 4 : 2;
-};
-
-// LDS address of the 16-byte piece p8 (0..7) of activation column a in one
-// 32-column x 128-byte stage tile: XOR swizzle so that 16 consecutive lanes
-// reading the same piece of 16 columns hit different banks.
-__device__ __forceinline__ uint32_t x_lds_off(int a, int p8) {
-    return (uint32_t)(a * 128 + 16 * (p8 ^ ((a >> 1) & 7)));
-}
-
-template <int TP16>
+template <int TP16, bool SC>
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, int ntiles) {
     constexpr int NT = (TP16 + 1) / 2;
-    constexpr int D = TileRing<NT>::depth;
     constexpr int kLastValues = (TP16 & 1) ? 8 : 16;
-    __shared__ __align__(16) unsigned char x_lds[2][NT][32 * 128];
+    constexpr int kStageBytes = NT * kXTileBytes;                 // one stage's activations
+    constexpr int kBlockBytes = kBlockStages * kStageBytes;       // one block's
+    constexpr int kXLoads = kBlockBytes / kLdsDmaBytes / kTileStrips;  // direct loads per wave per block
+    constexpr int LW = SC ? 2 : 4;                                // loads per stage (weights [+ scales])
+    constexpr int LX = kXLoads;                                   // activation loads per block
+    constexpr int LS = SC ? 1 : 0;                                // scale-chunk loads per block
+    // one array per buffer, so each buffer's direct loads are told apart
+    __shared__ __align__(16) unsigned char xb0[kBlockBytes];
+    __shared__ __align__(16) unsigned char xb1[kBlockBytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = (int)(K / kGroup);
-    const int nst = (G + 1) >> 1;  // stages per tile (the last one holds 1 group when G is odd)
+    const int nst = (G + 1) >> 1;                                 // real stages per tile
+    const int nbt = (nst + kBlockStages - 1) / kBlockStages;      // blocks per tile
     const int my_tiles = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int nq = my_tiles * nst;  // stages this workgroup processes
+    const int nb = my_tiles * nbt;                                // blocks of this workgroup
     const int r = lane & 31, c = lane >> 5;
 
     const __amdgpu_buffer_rsrc_t w_rsrc =
@@ -417,64 +423,74 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(N * G * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(S), (short)0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t x_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, 0, 0x00020000);
 
-    // this wave's share of each activation stage: columns 4 w .. 4 w + 3,
-    // lane l -> column 4 w + (l >> 4), bytes 8 (l & 15) .. + 8 of the 128
-    const int xa = 4 * wave + (lane >> 4);
-    uint32_t xg_off[NT];
-    uint32_t xl_off[NT];
+    // direct load i of this wave covers load m = kXLoads * wave + i of the
+    // block: stage m / (4 NT), tile (m / 4) % NT, columns 8 (m % 4) .. + 7
+    // (sized for two tiles: see xd_off in the split kernel)
+    uint32_t xg_off[4];
+    uint32_t xl_off[4];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        const int j = 32 * tt + xa;
-        const int jc = j < t ? j : t - 1;
-        xg_off[tt] = (uint32_t)(jc * ldx) * 2u + 8u * (lane & 15);
-        xl_off[tt] = (uint32_t)(tt * 32 * 128) + x_lds_off(xa, (lane & 15) >> 1) + 8u * (lane & 1);
+    for (int i = 0; i < kXLoads; ++i) {
+        const int m = kXLoads * wave + i;
+        const int st = m / (4 * NT), tt = (m / 4) % NT;
+        const int a = 32 * tt + 8 * (m % 4) + (lane >> 3);
+        const int jc = a < t ? a : t - 1;
+        xg_off[i] = (uint32_t)(jc * ldx) * 2u + (uint32_t)st * 64u * 2u + 16u * ((lane & 7) ^ ((lane >> 3) & 7));
+        xl_off[i] = (uint32_t)(st * kStageBytes + tt * kXTileBytes + (8 * (m % 4)) * 128);
     }
+
+    // tile of block b, first group of block b (wave-uniform)
+    auto tile_of = [&](int b) { return (int)blockIdx.x + (b / nbt) * (int)gridDim.x; };
+    auto strip_row = [&](int b) { return (int64_t)tile_of(b) * (kTileStrips * kRows) + (int64_t)wave * kRows; };
+    auto block_g = [&](int b) { return kBlockStages * 2 * (b % nbt); };
 
     struct WStage {
         u32x4 w[2];
         uint16_t s[2];
-        uint32_t x[NT][2];
     };
-    // tile and stage of global stage index q (wave-uniform)
-    auto tile_of = [&](int q) { return (int)blockIdx.x + (q / nst) * (int)gridDim.x; };
-    auto load = [&](int q, WStage& st) {
-        const int qc = q < nq ? q : nq - 1;  // past the end: repeat the last stage (cached)
-        const int tile = tile_of(qc);
-        const int g = 2 * (qc % nst);
+    // weights (and per-stage scales) of stage u of block b
+    auto load_stage = [&](int b, int u, WStage& st) {
+        const int g = block_g(b) + 2 * u;
+        const bool live = b < nb && g < G;
+        const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
         const int g1 = g + 1 < G ? g + 1 : g;  // odd G: the last stage repeats its group
-        const int64_t strip_row = (int64_t)tile * (kTileStrips * kRows) + (int64_t)wave * kRows;
+        const int64_t row0 = strip_row(b < nb ? b : nb - 1);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            int64_t row = strip_row + 16 * i + (lane & 15);
+            int64_t row = row0 + 16 * i + (lane & 15);
             row = row < N ? row : N - 1;
             const int gl = ((lane >> 4) & 1) ? g1 : g;
             const uint32_t off = (uint32_t)(row * K) + (uint32_t)gl * kGroup + 16u * (lane >> 5);
-            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, off, 0, 0));
+            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
         }
-        {
-            int64_t row = strip_row + r;
+        if constexpr (!SC) {
+            const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
+            int64_t row = row0 + r;
             row = row < N ? row : N - 1;
             const uint32_t off = (uint32_t)(row * G) * 2u;
-            st.s[0] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, off + 2u * g, 0, 0);
-            st.s[1] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, off + 2u * g1, 0, 0);
-        }
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            // second group's half of the 128-byte stage row (g1 == g repeats it)
-            const uint32_t goff = (lane & 8) ? (uint32_t)g1 * 64u - 64u : (uint32_t)g * 64u;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(x_rsrc, xg_off[tt] + goff, 0, 0);
-            st.x[tt][0] = v[0];
-            st.x[tt][1] = v[1];
+            st.s[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, off + 2u * g, 0, 0);
+            st.s[1] = __builtin_amdgcn_raw_buffer_load_b16(sr, off + 2u * g1, 0, 0);
         }
     };
-    auto write_x = [&](const WStage& st, int slot) {
+    // this lane's row's 8 scales of block b (SC)
+    auto load_scales = [&](int b) -> u32x4 {
+        const bool live = b < nb;
+        int64_t row = strip_row(live ? b : nb - 1) + r;
+        row = row < N ? row : N - 1;
+        const uint32_t off = (uint32_t)(row * G + block_g(b < nb ? b : nb - 1)) * 2u;
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? s_rsrc : s_none, off, 0, 0));
+    };
+    // this wave's share of block b's activations, into buffer xb
+    auto load_x = [&](int b, unsigned char* xb) {
+        const bool live = b < nb;
+        const uint32_t g_off = (uint32_t)block_g(live ? b : nb - 1) * 64u;
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            uint32_t* p = reinterpret_cast<uint32_t*>(&x_lds[slot][0][0] + xl_off[tt]);
-            p[0] = st.x[tt][0];
-            p[1] = st.x[tt][1];
-        }
+        for (int i = 0; i < kXLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? x_rsrc : x_none, W8I_LDS(xb + xl_off[i]), 16,
+                                                     xg_off[i] + g_off, 0, 0, 0);
     };
 
     double acc[NT][16], total[NT][16];
@@ -482,12 +498,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[tt][v] = total[tt][v] = 0.0;
-
-    WStage ring[D];
-#pragma unroll
-    for (int u = 0; u < D; ++u) load(u, ring[u]);
-    write_x(ring[0], 0);
-    __syncthreads();
 
     // `slice` is the slice the next group belongs to; a slice is folded into
     // the running total as soon as the groups before the next stage are done
@@ -503,43 +513,84 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             }
         ++slice;
     };
-    // one stage: q is the global stage index, `cur` its ring slot and `nxt`
-    // the slot of stage q + 1 (whose activations are published now)
-    auto stage = [&](int q, WStage& cur, const WStage& nxt) {
-        write_x(nxt, (q + 1) & 1);
-        swap16(cur.w[0], cur.w[1]);
-        const int g = 2 * (q % nst);
-        const int ng = (g + 1 < G) ? 2 : 1;
-        if (kslice_begin(G, slice + 1) <= g) {
-            do fold_slice();
-            while (kslice_begin(G, slice + 1) <= g);
-        }
-        const unsigned char* xs = &x_lds[q & 1][0][0];
+
+    WStage ring[kBlockStages];
+    u32x4 sc0 = {}, sc1 = {};
+    // prologue: block 0's activations, scales and weights, in this order (the
+    // wait counts below depend on it; the scheduling barriers keep it)
+    load_x(0, xb0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SC) sc0 = load_scales(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int gs = 0; gs < 2; ++gs) {
-            if (gs >= ng) break;  // odd G: the tile's last stage has one group
-            const bf16x8 b_lo = dequant8(cur.w[gs].x, cur.w[gs].y);
-            const bf16x8 b_hi = dequant8(cur.w[gs].z, cur.w[gs].w);
-            const double sc = (double)(float)__builtin_bit_cast(_Float16, cur.s[gs]);
+    for (int u = 0; u < kBlockStages; ++u) {
+        load_stage(0, u, ring[u]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // block b: activations in xs, scales in sc; block b + 1 is loaded into
+    // xn and sn.  Blocks go in pairs so that buffers and scale registers are
+    // named statically; a phantom block pads an odd count.
+    auto block = [&](int b, const unsigned char* xs, unsigned char* xn, const u32x4& sc, u32x4& sn) {
+        // this wave's direct loads of block b have landed once only the loads
+        // issued after them are pending; the barrier publishes all waves'
+        wait_vm<LS + kBlockStages * LW>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // every wave is past block b - 1, so its buffer takes block b + 1
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(b + 1, xn);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SC) sn = load_scales(b + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool live = b < nb;
+        const int g0 = block_g(b);
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const u32x4 a0 =
-                    *reinterpret_cast<const u32x4*>(xs + tt * 32 * 128 + x_lds_off(r, 4 * gs + 2 * c));
-                const u32x4 a1 =
-                    *reinterpret_cast<const u32x4*>(xs + tt * 32 * 128 + x_lds_off(r, 4 * gs + 2 * c + 1));
-                const f32x16 zero = {};
-                f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo, zero, 0,
-                                                                   0, 0);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
-                const int nv = (tt == NT - 1) ? kLastValues : 16;
+        for (int u = 0; u < kBlockStages; ++u) {
+            // stage u's loads have landed once only the loads issued after
+            // them are pending (the same count for every stage)
+            wait_vm<(kBlockStages - 1) * LW + LX + LS>();
+            WStage& cur = ring[u];
+            const int g = g0 + 2 * u;
+            if (live && g < G) {
+                swap16(cur.w[0], cur.w[1]);
+                while (kslice_begin(G, slice + 1) <= g) fold_slice();
+                const int ng = (g + 1 < G) ? 2 : 1;
 #pragma unroll
-                for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc, (double)d[v], acc[tt][v]);
+                for (int gs = 0; gs < 2; ++gs) {
+                    if (gs >= ng) break;  // odd G: the tile's last stage has one group
+                    const bf16x8 b_lo = dequant8(cur.w[gs].x, cur.w[gs].y);
+                    const bf16x8 b_hi = dequant8(cur.w[gs].z, cur.w[gs].w);
+                    uint16_t s16;
+                    if constexpr (SC)
+                        s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
+                    else
+                        s16 = cur.s[gs];
+                    const double scale = (double)(float)__builtin_bit_cast(_Float16, s16);
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const unsigned char* xt = xs + u * kStageBytes + tt * kXTileBytes;
+                        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c));
+                        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c + 1));
+                        const f32x16 zero = {};
+                        f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo,
+                                                                           zero, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
+                        const int nv = (tt == NT - 1) ? kLastValues : 16;
+#pragma unroll
+                        for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(scale, (double)d[v], acc[tt][v]);
+                    }
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            load_stage(b + 1, u, cur);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (g + ng == G) {
-            // the tile's last stage: fold the remaining slices, store this strip
+        if (live && b % nbt == nbt - 1) {
+            // the tile's last block: fold the remaining slices, store this strip
             while (slice < kKSlices) fold_slice();
-            const int64_t n = (int64_t)tile_of(q) * (kTileStrips * kRows) + (int64_t)wave * kRows + r;
+            const int64_t n = strip_row(b) + r;
             if (n < N) {
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt)
@@ -551,30 +602,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             }
             slice = 0;
         }
-        load(q + D, cur);
-        __syncthreads();
     };
-
-    // full blocks of D stages (no exits inside, so the wait counts stay
-    // exact), then the remaining stages
-    const int nblocks = nq / D;
-    int q = 0;
-    for (int blk = 0; blk < nblocks; ++blk, q += D) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) stage(q + u, ring[u], ring[(u + 1) % D]);
+    for (int b = 0; b < nb; b += 2) {
+        block(b, xb0, xb1, sc0, sc1);
+        block(b + 1, xb1, xb0, sc1, sc0);
     }
-    switch (nq - nblocks * D) {
-#define W8I_TILE_TAIL(R)                                                         \
-    case R:                                                                      \
-        _Pragma("unroll") for (int u = 0; u < R; ++u) stage(q + u, ring[u], ring[(u + 1) % D]); \
-        break;
-        W8I_TILE_TAIL(1)
-        W8I_TILE_TAIL(2)
-        W8I_TILE_TAIL(3)
-#undef W8I_TILE_TAIL
-        default:
-            break;
-    }
+    // the phantom block's loads are still in flight: drain them before exit
+    wait_vm<0>();
 }
 
 // Tiles of the persistent kernel; it is used when there are enough of them
@@ -582,7 +616,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
 static int tile_count(int64_t N) { return (int)((N + kTileStrips * kRows - 1) / (kTileStrips * kRows)); }
 
 static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
-                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, bool sc, hipStream_t stream) {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -591,10 +625,20 @@ static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, i
     const dim3 grid((unsigned)(ntiles < ncu ? ntiles : ncu)), block(kGemmThreads);
     switch (T_pad / 16) {
         case 1:
-            hipLaunchKernelGGL(gemm_w8g32_tiles<1>, grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, ntiles);
+            if (sc)
+                hipLaunchKernelGGL((gemm_w8g32_tiles<1, true>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
+                                   ntiles);
+            else
+                hipLaunchKernelGGL((gemm_w8g32_tiles<1, false>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
+                                   ntiles);
             break;
         case 2:
-            hipLaunchKernelGGL(gemm_w8g32_tiles<2>, grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, ntiles);
+            if (sc)
+                hipLaunchKernelGGL((gemm_w8g32_tiles<2, true>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
+                                   ntiles);
+            else
+                hipLaunchKernelGGL((gemm_w8g32_tiles<2, false>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
+                                   ntiles);
             break;
         default:
             return W8I_ET;
@@ -610,12 +654,16 @@ struct LinearPlan {
     LinearKernel kind;
     int tp16;         // T_pad / 16
     int depth;        // ring depth of the LDS-staged split kernel
-    bool lds_scales;  // ... and whether it copies the scales to LDS
+    bool lds_scales;  // ... and whether it copies the scales to LDS; for the
+                      // tiles kernel: whether it loads the scales by blocks
 };
 
 static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
     const int tp16 = T_pad / 16;
-    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return {LinearKernel::kTiles, tp16, 0, false};
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) {
+        const bool sc = (K / kGroup) % 8 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+        return {LinearKernel::kTiles, tp16, 0, sc};
+    }
     // the LDS-staged variant: with the deepest ring (3 or 2 stages for one
     // 32-column tile, 2 for two) whose LDS leaves room for the strip's scales
     // when they can be copied as 16-byte pieces (scales 16-byte aligned);
@@ -633,7 +681,8 @@ static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
 }
 
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
-    static const char* const tiles[] = {"gemm_w8g32_tiles<1>", "gemm_w8g32_tiles<2>"};
+    static const char* const tiles[2][2] = {{"gemm_w8g32_tiles<1, false>", "gemm_w8g32_tiles<1, true>"},
+                                            {"gemm_w8g32_tiles<2, false>", "gemm_w8g32_tiles<2, true>"}};
     static const char* const split_lds[4][3] = {
         {"gemm_w8g32_split_lds<1, 2, true>", "gemm_w8g32_split_lds<1, 3, true>", ""},
         {"gemm_w8g32_split_lds<2, 2, true>", "gemm_w8g32_split_lds<2, 3, true>", ""},
@@ -644,7 +693,7 @@ const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
     const LinearPlan p = plan_linear(N, K, T_pad, S);
     switch (p.kind) {
-        case LinearKernel::kTiles: return tiles[p.tp16 - 1];
+        case LinearKernel::kTiles: return tiles[p.tp16 - 1][p.lds_scales ? 1 : 0];
         case LinearKernel::kSplitLds:
             return p.lds_scales ? split_lds[p.tp16 - 1][p.depth - 2] : split_lds_gs[p.tp16 - 1];
         default: return "";
@@ -658,7 +707,7 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
     const dim3 block(kGemmThreads);
     switch (p.kind) {
         case LinearKernel::kTiles:
-            return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, stream);
+            return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, p.lds_scales, stream);
         case LinearKernel::kSplitLds: {
 #define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                  \
     case TP * 16 + D * 2 + LS:                                                                       \

@@ -32,7 +32,9 @@ def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
     q = L.w8_linear_invariant_kernel
     assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true>"
     assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false>"  # scales not 16-byte aligned
-    assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2>"
+    assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2, true>"
+    assert q(248320, 5120, 32, fake(4098)) == b"gemm_w8g32_tiles<2, false>"   # scales not 16-byte aligned
+    assert q(248320, 5088, 16, fake(4096)) == b"gemm_w8g32_tiles<1, false>"   # K/32 = 159
     assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true>"
     assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false>"  # scales too large for LDS
     for bad in ((6144, 5100, 32), (0, 5120, 32), (6144, 5120, 24), (6144, 5120, 80)):

@@ -253,7 +253,8 @@ def test_mlp_projections_t_values():
 LARGE = [  # N, K, T_pad: N >= 131072 selects the persistent kernel for T_pad <= 32
     (131072 + 100, 1024, 32),
     (131072 + 33, 96, 16),      # K/32 = 3: odd group count, seven empty slices
-    (131072 + 256, 5120, 32),
+    (131072 + 256, 5120, 32),   # K/32 = 160: scales loaded 8 groups at a time
+    (131072 + 77, 5088, 32),    # K/32 = 159: scales loaded per stage, odd group count
 ]
 
 
