@@ -106,12 +106,16 @@ __host__ __device__ constexpr int split_lds_scale_bytes(int NT, int D) {
     return (int)kMaxGemmLds - D * split_lds_slot_bytes(NT) - (4 - D) * 16;
 }
 
-// Byte offset of 16-byte piece p (0..7) of column a inside a wave's stage:
-// XOR swizzle, so that 8 consecutive columns reading one piece hit 8
-// different bank groups.  Direct load i, lane l fills bytes 16 l .. 16 l + 15
-// of the instruction's kilobyte, which is column 8 i + (l >> 3), piece
-// (l & 7) ^ ((l >> 3) & 7).
-__device__ __forceinline__ uint32_t xs_off(int a, int p) { return (uint32_t)(a * 128 + 16 * (p ^ (a & 7))); }
+// Byte offset of 16-byte piece p (0..7) of column a inside a stage: XOR
+// swizzle.  The LDS serves a 16-byte read of 16 lanes (256 bytes, 64 banks)
+// per pass; 16 consecutive columns reading one piece land in 16 different
+// bank groups because the slot is p ^ ((a >> 1) & 7) and a * 128 alternates
+// the 128-byte halves.  (With p ^ (a & 7), columns a and a + 8 collided: the
+// counters showed half of all LDS cycles as bank conflicts.)  A direct load
+// whose lane l fills bytes 16 l .. 16 l + 15 of 8 columns therefore fetches
+// piece xs_piece(a, l) of its column a.
+__device__ __forceinline__ uint32_t xs_off(int a, int p) { return (uint32_t)(a * 128 + 16 * (p ^ ((a >> 1) & 7))); }
+__device__ __forceinline__ uint32_t xs_piece(int a, int lane) { return (uint32_t)((lane & 7) ^ ((a >> 1) & 7)); }
 
 // s_waitcnt that waits until at most N vector-memory operations are pending
 template <int N>
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     for (int i = 0; i < kXLoads; ++i) {
         const int a = 8 * i + (lane >> 3);
         const int jc = a < t ? a : t - 1;
-        xd_off[i] = (uint32_t)(jc * ldx) * 2u + 16u * ((lane & 7) ^ ((lane >> 3) & 7));
+        xd_off[i] = (uint32_t)(jc * ldx) * 2u + 16u * xs_piece(a, lane);
     }
     const int r = lane & 31;  // weight row of this lane after the swaps (B column, D column)
     const int c = lane >> 5;
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         const int st = m / (4 * NT), tt = (m / 4) % NT;
         const int a = 32 * tt + 8 * (m % 4) + (lane >> 3);
         const int jc = a < t ? a : t - 1;
-        xg_off[i] = (uint32_t)(jc * ldx) * 2u + (uint32_t)st * 64u * 2u + 16u * ((lane & 7) ^ ((lane >> 3) & 7));
+        xg_off[i] = (uint32_t)(jc * ldx) * 2u + (uint32_t)st * 64u * 2u + 16u * xs_piece(a, lane);
         xl_off[i] = (uint32_t)(st * kStageBytes + tt * kXTileBytes + (8 * (m % 4)) * 128);
     }
 
