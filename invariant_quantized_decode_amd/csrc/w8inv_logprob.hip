@@ -102,14 +102,40 @@ __global__ __launch_bounds__(kLpThreads) void lp_block_max(const uint16_t* __res
 }
 
 // max over the block maxima of column j (NaN if any block saw a NaN)
+// Row max of column j from its nb block maxima, by all threads of the
+// workgroup (NTH threads, NTH / 64 waves) at once: a max is exact in any
+// order.  (A +0 / -0 tie may resolve either way; no output bit depends on
+// it: the max only enters through l - m, and its sign could matter only for
+// a unique maximum.)  nan is set when any block max is NaN.
+template <int NTH>
 __device__ __forceinline__ float row_max_from_blocks(const float* M, int nb, int j, bool& nan) {
+    __shared__ float wmax[NTH / 64];
+    __shared__ int wnan[NTH / 64];
     float m = -__builtin_inff();
-    nan = false;
-    for (int i = 0; i < nb; ++i) {
+    int n = 0;
+    for (int i = threadIdx.x; i < nb; i += NTH) {
         const float v = M[(int64_t)j * nb + i];
-        if (v != v) nan = true;
+        if (v != v) n = 1;
         else m = __builtin_fmaxf(m, v);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        m = __builtin_fmaxf(m, __shfl_xor(m, off));
+        n |= __shfl_xor(n, off);
+    }
+    if constexpr (NTH > 64) {
+        if ((threadIdx.x & 63) == 0) {
+            wmax[threadIdx.x >> 6] = m;
+            wnan[threadIdx.x >> 6] = n;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NTH / 64; ++w) {
+            m = __builtin_fmaxf(m, wmax[w]);
+            n |= wnan[w];
+        }
+    }
+    nan = n != 0;
     return m;
 }
 
@@ -120,20 +146,13 @@ __global__ __launch_bounds__(kLpThreads) void lp_block_sumexp(const uint16_t* __
     constexpr int C = E < 8 ? E : 8;
     constexpr int NC = E / C;
     __shared__ float wsum[kLpThreads / 64];
-    __shared__ float s_max;
-    __shared__ int s_nan;
     const int b = blockIdx.x, j = blockIdx.y;
-    if (threadIdx.x == 0) {
-        bool nan;
-        s_max = row_max_from_blocks(M, nb, j, nan);
-        s_nan = nan;
-    }
-    __syncthreads();
-    if (s_nan) {
+    bool nan;
+    const float m = row_max_from_blocks<kLpThreads>(M, nb, j, nan);
+    if (nan) {
         if (threadIdx.x == 0) P[(int64_t)j * nb + b] = __builtin_nanf("");
         return;
     }
-    const float m = s_max;
     const uint16_t* row = L + (int64_t)j * ldl;
     const int64_t base = (int64_t)b * (E * kLpThreads) + (int64_t)threadIdx.x * E;
 
@@ -168,15 +187,39 @@ __global__ __launch_bounds__(kLpThreads) void lp_block_sumexp(const uint16_t* __
     if (threadIdx.x == 0) P[(int64_t)j * nb + b] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
-__global__ void lp_fold(const uint16_t* __restrict__ L, int64_t V, int64_t ldl, const int64_t* __restrict__ targets,
-                        int nb, const float* __restrict__ M, const float* __restrict__ P, float* __restrict__ out,
-                        int t) {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= t) return;
+// One wave per column: the block partials are staged in LDS by all lanes
+// (their loads in flight together), then lane 0 folds them left to right.
+constexpr int kFoldChunk = 1024;  // partials staged per pass
+__global__ __launch_bounds__(64) void lp_fold(const uint16_t* __restrict__ L, int64_t V, int64_t ldl,
+                                               const int64_t* __restrict__ targets, int nb,
+                                               const float* __restrict__ M, const float* __restrict__ P,
+                                               float* __restrict__ out) {
+    __shared__ __align__(16) float part[kFoldChunk];
+    const int j = blockIdx.x;
+    const int lane = threadIdx.x;
     bool nan;
-    const float m = row_max_from_blocks(M, nb, j, nan);
-    float S = P[(int64_t)j * nb];
-    for (int b = 1; b < nb; ++b) S = S + P[(int64_t)j * nb + b];
+    const float m = row_max_from_blocks<64>(M, nb, j, nan);
+    float S = 0.0f;
+    for (int b0 = 0; b0 < nb; b0 += kFoldChunk) {
+        const int n = nb - b0 < kFoldChunk ? nb - b0 : kFoldChunk;
+        for (int i = lane; i < n; i += 64) part[i] = P[(int64_t)j * nb + b0 + i];
+        __syncthreads();
+        if (lane == 0) {
+            // S = ((P_0 + P_1) + P_2) + ... in vocabulary order
+            int i = 0;
+            if (b0 == 0) S = part[i++];
+            for (; i + 4 <= n; i += 4) {  // four reads in flight, adds in order
+                const float p0 = part[i], p1 = part[i + 1], p2 = part[i + 2], p3 = part[i + 3];
+                S = S + p0;
+                S = S + p1;
+                S = S + p2;
+                S = S + p3;
+            }
+            for (; i < n; ++i) S = S + part[i];
+        }
+        __syncthreads();
+    }
+    if (lane != 0) return;
     const int64_t tg = targets[j];
     if (nan || tg < 0 || tg >= V) {
         out[j] = __builtin_nanf("");
@@ -228,7 +271,7 @@ int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* 
         case 128: launch_lp_e<128>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
         default: return W8I_EBLOCK;
     }
-    hipLaunchKernelGGL(lp_fold, dim3((t + 63) / 64), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out, t);
+    hipLaunchKernelGGL(lp_fold, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 
