@@ -8,7 +8,7 @@ Infinity Cache cannot serve them, steps are replayed from HIP graphs, and the
 time of the timed steps is taken with HIP events on the stream they run on.
 The same is measured at t = 1.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1] [--pmc-pass]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1] [--pmc-pass] [--all]
 """
 from __future__ import annotations
 
@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=330)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--all", action="store_true",
+                   help="instead of the bench line: one JSON line per workload (every configured projection and "
+                        "the chain's, at t=1 and t=T_pad, and the head's logprob), with the CPU oracle on a row sample")
     p.add_argument("--pmc-pass", action="store_true",
                    help="for rocprofv3 --pmc: a few plain launches at t=T_pad and t=1, then a plain 512 MiB "
                         "device copy (the calibration for the HBM byte counters); prints one short JSON line")
@@ -56,6 +59,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.all:
+        run_all(torch, w8, synth, dev, args)
+        return
     case = synth.LINEAR_6144
     N, K, T_pad = case.N, case.K, case.T_pad
     d = synth.linear_6144_permuted()
@@ -217,6 +223,99 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def run_all(torch, w8, synth, dev, args):
+    """Per-workload figures (context for the bench line): synthetic inputs with the configured value
+    distributions drawn on the device, weights rotating over >= 1 GiB of copies, graph-replayed
+    launches timed with HIP events on their stream."""
+    import oracle
+
+    chain = [("chain qkv 7168x5120", 7168, 5120), ("chain o 5120x6144", 5120, 6144),
+             ("chain gate+up 34816x5120", 34816, 5120), ("chain down 5120x17408", 5120, 17408)]
+    work = [(c.name, c.N, c.K, c.T_pad, c.scale_eps) for c in
+            (synth.LINEAR_1024, synth.LINEAR_6144, synth.MLP_GATE_UP, synth.MLP_DOWN, synth.HEAD)]
+    work += [(n, N, K, synth.CHAIN_T_PAD, 0.0) for n, N, K in chain]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    stream = torch.cuda.Stream(device=dev)
+    for name, N, K, T_pad, eps in work:
+        wbytes = N * K + 2 * N * (K // 32)
+        copies = max(1, math.ceil((1 << 30) / wbytes))
+        Ws = [torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8, device=dev) for _ in range(copies)]
+        Ss = [(torch.randn(N, K // 32, generator=g, device=dev).abs_() * 0.02 + eps).half() for _ in range(copies)]
+        X = torch.randn(T_pad, K, generator=g, device=dev).to(torch.bfloat16)
+        Y = torch.empty((T_pad, N), dtype=torch.bfloat16, device=dev)
+        kernel = w8.w8_linear_invariant_kernel(N, K, T_pad, Ss[0])
+        for t in (1, T_pad):
+            reps = max(2, math.ceil(20000 / copies))  # about 20000 launches, fewer for the largest
+            reps = min(reps, max(2, int(2e10 // (wbytes * copies))))
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                w8.w8_linear_invariant(Ws[0], Ss[0], X[:t], t, T_pad, y=Y)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=stream):
+                    for i in range(copies):
+                        w8.w8_linear_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)
+                graph.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    graph.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 1e3 / (reps * copies)
+            alg = wbytes + 2 * t * (K + N)
+            # CPU oracle on a 64-row sample of the same projection
+            rows = np.arange(0, N, max(1, N // 64))[:64]
+            qh = Ws[0][rows].cpu().numpy()
+            sh = Ss[0][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+            xh = X[:t].view(torch.int16).cpu().numpy().view(np.uint16)
+            c0 = time.perf_counter()
+            oracle.w8_linear(qh, sh, xh)
+            csec = time.perf_counter() - c0
+            print(json.dumps({"workload": name, "kernel": kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
+                              "weight_gbs": round(wbytes / sec / 1e9, 1),
+                              "roofline_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
+                              "tflops_useful": round(2.0 * N * K * t / sec / 1e12, 3),
+                              "cpu_oracle_gbs": round(len(rows) * K * 1.0625 / csec / 1e9, 4),
+                              "cpu_sample": f"{len(rows)} rows, {oracle.max_threads()} threads"}), flush=True)
+        del Ws, Ss
+        torch.cuda.empty_cache()
+    # the head's logprob epilogue
+    V, block = synth.HEAD.N, synth.HEAD_BLOCK
+    for t in (1, synth.HEAD.T_pad):
+        logits = (torch.randn(t, V, generator=g, device=dev) * 105).to(torch.bfloat16)
+        targets = torch.randint(0, V, (t,), generator=g, device=dev, dtype=torch.int64)
+        ws = torch.empty(w8.vocab_block_logprob_workspace_bytes(t, V, block), dtype=torch.uint8, device=dev)
+        out = torch.empty(t, dtype=torch.float32, device=dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            w8.vocab_block_logprob(logits, targets, block, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(20):
+                    w8.vocab_block_logprob(logits, targets, block, out=out, workspace=ws)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(50):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / 1000
+        nb = (V + block - 1) // block
+        alg = 2 * (2 * t * V) + 8 * t * nb
+        lh = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        c0 = time.perf_counter()
+        oracle.block_logprob(lh, targets.cpu().numpy(), block)
+        csec = time.perf_counter() - c0
+        print(json.dumps({"workload": f"vocab block logprob V={V} block={block}", "kernel": "lp_block_max/sumexp/fold",
+                          "t": t, "us": round(sec * 1e6, 2), "alg_gbs": round(alg / sec / 1e9, 1),
+                          "roofline_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
+                          "cpu_oracle_us": round(csec * 1e6, 1)}), flush=True)
 
 
 if __name__ == "__main__":
