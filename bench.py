@@ -283,6 +283,33 @@ def run_all(torch, w8, synth, dev, args):
                               "cpu_sample": f"{len(rows)} rows, {oracle.max_threads()} threads"}), flush=True)
         del Ws, Ss
         torch.cuda.empty_cache()
+    # the chain's column-local glue at T_pad columns (graph-replayed; bytes = reads + writes)
+    H, F, tg = synth.CHAIN_HIDDEN, synth.CHAIN_FFN, synth.CHAIN_T_PAD
+    xg = torch.randn(tg, H, generator=g, device=dev).to(torch.bfloat16)
+    gu = (torch.randn(tg, 2 * F, generator=g, device=dev) * 30).to(torch.bfloat16)
+    yh, yf = torch.empty_like(xg), torch.empty((tg, F), dtype=torch.bfloat16, device=dev)
+    for gname, fn, nbytes in (("rmsnorm", lambda: w8.w8i_rmsnorm(xg, 1e-6, y=yh), 2 * 2 * tg * H),
+                              ("swiglu", lambda: w8.w8i_swiglu(gu, y=yf), 3 * 2 * tg * F),
+                              ("residual add", lambda: w8.w8i_residual_add(xg, xg, y=yh), 3 * 2 * tg * H)):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(50):
+                    fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / 1000
+        print(json.dumps({"workload": f"glue {gname} t={tg} H={H} F={F}", "us": round(sec * 1e6, 2),
+                          "alg_gbs": round(nbytes / sec / 1e9, 1),
+                          "roofline_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
     # the head's logprob epilogue
     V, block = synth.HEAD.N, synth.HEAD_BLOCK
     for t in (1, synth.HEAD.T_pad):
