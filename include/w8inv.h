@@ -104,6 +104,41 @@ int w8_linear_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_
 const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t *scales);
 
 /* ---------------------------------------------------------------------------
+ * Fused W8 projection epilogues.
+ *
+ * Source: the ninfer issue (GitHub issue 80), table "Where t selects
+ * arithmetic", row "attn_input_proj, linear_swiglu, linear_pair, linear_add
+ * (W8)": the fused decode ops run the W8 linear's main loop with an epilogue.
+ * Here they run the same K plan as w8_linear_invariant, so every projection
+ * output has that call's bits, and the epilogue is the glue call's arithmetic:
+ *
+ *   w8_linear_add_invariant:    y = w8i_residual_add(w8_linear_invariant(x), residual)
+ *   w8_linear_swiglu_invariant: y = w8i_swiglu(w8_linear_invariant(x))
+ *
+ * bit for bit, with the 34816-wide (say) intermediate never written.  Both
+ * always run the LDS-staged split kernel.  Operands, T_pad, t, K, ldx, the
+ * alignment rules and the errors are those of w8_linear_invariant; no
+ * workspace is needed.
+ *
+ * w8_linear_add_invariant: W_q [N, K], scales [N, K/32], residual bf16
+ *   [t, ldr] (2-byte aligned, ldr >= N), y bf16 [t, ldy].  y may be the
+ *   residual itself (same pointer and ldr == ldy: each element is read before
+ *   it is written); any other overlap is W8I_ESHAPE.
+ * w8_linear_swiglu_invariant: W_q [2F, K], scales [2F, K/32]: rows [0, F) are
+ *   the gate projection, rows [F, 2F) the up projection (the layout whose
+ *   output w8i_swiglu takes).  y bf16 [t, ldy], ldy >= F:
+ *   y[j, h] = silu(gate[j, h]) * up[j, h] as w8i_swiglu computes it from the
+ *   two bf16-rounded projection outputs.  2F * K < 2^32.
+ * ------------------------------------------------------------------------- */
+int w8_linear_add_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_t *x,
+                            const uint16_t *residual, int32_t t, int32_t T_pad, uint16_t *y,
+                            int64_t N, int64_t K, int64_t ldx, int64_t ldr, int64_t ldy, void *stream);
+
+int w8_linear_swiglu_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_t *x,
+                               int32_t t, int32_t T_pad, uint16_t *y, int64_t F, int64_t K,
+                               int64_t ldx, int64_t ldy, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Target-token logprob by fixed-width vocabulary blocks (LM-head epilogue).
  *
  * Source: the tokenspeed "Numerics envelopes" page, alignment.trainer table

@@ -25,7 +25,8 @@ STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: 
           -6: "W8I_EWORKSPACE", -7: "W8I_EHIP"}
 
 EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
-           "w8_linear_invariant_kernel", "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
+           "w8_linear_invariant_kernel", "w8_linear_add_invariant", "w8_linear_swiglu_invariant",
+           "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32")
 
 
@@ -47,6 +48,8 @@ def _load():
     L.w8_linear_invariant.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
     L.w8_linear_invariant.restype = ctypes.c_int
     L.w8_linear_invariant_kernel.argtypes, L.w8_linear_invariant_kernel.restype = [I64, I64, I32, P], ctypes.c_char_p
+    L.w8_linear_add_invariant.argtypes = [P, P, P, P, I32, I32, P, I64, I64, I64, I64, I64, P]
+    L.w8_linear_swiglu_invariant.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
     L.vocab_block_logprob_workspace_bytes.argtypes = [I32, I64, I32]
     L.vocab_block_logprob_workspace_bytes.restype = SZ
     L.vocab_block_logprob.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
@@ -56,7 +59,7 @@ def _load():
     L.w8i_residual_add.argtypes = [P, P, P, I32, I64, I64, I64, I64, P]
     L.w8i_exp32.argtypes = [P, P, I64, P]
     L.w8i_log32.argtypes = [P, P, I64, P]
-    for name in ("w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
+    for name in ("w8_linear_add_invariant", "w8_linear_swiglu_invariant", "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -111,12 +114,7 @@ def version() -> str:
     return _lib.w8i_version().decode()
 
 
-def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, t: int, T_pad: int,
-                        y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[:t] = bf16(dequant(W_q, scales) @ x[:t]^T) at the fixed width T_pad.
-
-    W_q int8 [N, K]; scales fp16 [N, K/32]; x bf16 [>=t, K] (token rows); y bf16 [t, N] (allocated if None).
-    """
+def _projection_args(W_q, scales, x, t, y, y_cols):
     if W_q.dtype != torch.int8 or W_q.dim() != 2 or not W_q.is_contiguous():
         raise ValueError("W_q must be a contiguous int8 [N, K] tensor")
     N, K = W_q.shape
@@ -127,14 +125,51 @@ def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor
         raise ValueError("x must be a bf16 [>=t, K] tensor")
     ldx = _row_major(x, "x")
     if y is None:
-        y = torch.empty((t, N), dtype=torch.bfloat16, device=W_q.device)
-    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != N or y.size(0) < t:
-        raise ValueError("y must be a bf16 [>=t, N] tensor")
+        y = torch.empty((t, y_cols), dtype=torch.bfloat16, device=W_q.device)
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != y_cols or y.size(0) < t:
+        raise ValueError(f"y must be a bf16 [>=t, {y_cols}] tensor")
     ldy = _row_major(y, "y")
     _same_gpu(("W_q", W_q), ("scales", scales), ("x", x), ("y", y))
+    return N, K, ldx, y, ldy
+
+
+def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, t: int, T_pad: int,
+                        y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[:t] = bf16(dequant(W_q, scales) @ x[:t]^T) at the fixed width T_pad.
+
+    W_q int8 [N, K]; scales fp16 [N, K/32]; x bf16 [>=t, K] (token rows); y bf16 [t, N] (allocated if None).
+    """
+    N, K, ldx, y, ldy = _projection_args(W_q, scales, x, t, y, W_q.shape[0])
     st = _lib.w8_linear_invariant(_ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y), N, K, ldx, ldy,
                                   None, 0, ctypes.c_void_p(_stream(W_q.device)))
     _check("w8_linear_invariant", st)
+    return y
+
+
+def w8_linear_add_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, residual: torch.Tensor,
+                            t: int, T_pad: int, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[:t] = residual add of w8_linear_invariant(...) and residual[:t]; y may be `residual` itself."""
+    N, K, ldx, y, ldy = _projection_args(W_q, scales, x, t, y, W_q.shape[0])
+    _same_gpu(("W_q", W_q), ("residual", residual))
+    if residual.dtype != torch.bfloat16 or residual.dim() != 2 or residual.size(1) != N or residual.size(0) < t:
+        raise ValueError("residual must be a bf16 [>=t, N] tensor")
+    st = _lib.w8_linear_add_invariant(_ptr(W_q), _ptr(scales), _ptr(x), _ptr(residual), int(t), int(T_pad), _ptr(y),
+                                      N, K, ldx, _row_major(residual, "residual"), ldy,
+                                      ctypes.c_void_p(_stream(W_q.device)))
+    _check("w8_linear_add_invariant", st)
+    return y
+
+
+def w8_linear_swiglu_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, t: int, T_pad: int,
+                               y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[:t] = SwiGLU of the gate+up projection: W_q int8 [2F, K] (gate rows, then up rows); y bf16 [t, F]."""
+    if W_q.dim() != 2 or W_q.shape[0] % 2:
+        raise ValueError("W_q must be [2F, K]")
+    F = W_q.shape[0] // 2
+    N, K, ldx, y, ldy = _projection_args(W_q, scales, x, t, y, F)
+    st = _lib.w8_linear_swiglu_invariant(_ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y), F, K, ldx,
+                                         ldy, ctypes.c_void_p(_stream(W_q.device)))
+    _check("w8_linear_swiglu_invariant", st)
     return y
 
 

@@ -18,6 +18,22 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 40;
 
+// checks shared by the projections: the W8 operands of an [N, K] projection
+int check_projection(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, int32_t t, int32_t T_pad,
+                     const uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, int64_t y_cols) {
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
+    if (t < 0 || t > T_pad) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!W_q || !scales || !x || !y) return W8I_ENULL;
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return W8I_ESHAPE;
+    if (N * K >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (ldx < K || ldy < y_cols || ldx > ((int64_t)1 << 24)) return W8I_ESHAPE;
+    if (!aligned(W_q, 16) || !aligned(x, 16) || ldx % 8 != 0 || !aligned(scales, 2) || !aligned(y, 2))
+        return W8I_EALIGN;
+    if ((N + 31) / 32 > 0x7fffffffLL) return W8I_ESHAPE;
+    return W8I_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -50,22 +66,44 @@ int w8_linear_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_
                         size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
-    if (t < 0 || t > T_pad) return W8I_ET;
-    if (t == 0) return W8I_OK;
-    if (!W_q || !scales || !x || !y) return W8I_ENULL;
-    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return W8I_ESHAPE;
-    if (N * K >= ((int64_t)1 << 32)) return W8I_ESHAPE;  // per-lane 32-bit byte offsets
-    if (ldx < K || ldy < N || ldx > ((int64_t)1 << 24)) return W8I_ESHAPE;
-    if (!aligned(W_q, 16) || !aligned(x, 16) || ldx % 8 != 0 || !aligned(scales, 2) || !aligned(y, 2))
-        return W8I_EALIGN;
-    if ((N + 31) / 32 > 0x7fffffffLL) return W8I_ESHAPE;
+    const int st = check_projection(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, N);
+    if (st != W8I_OK || t == 0) return st;
     return launch_linear(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
 }
 
 const char* w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t* scales) {
     if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return "";
     return linear_kernel_name(N, K, T_pad, scales);
+}
+
+int w8_linear_add_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const uint16_t* residual,
+                            int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldr,
+                            int64_t ldy, void* stream) {
+    const int st = check_projection(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, N);
+    if (st != W8I_OK || t == 0) return st;
+    if (!residual) return W8I_ENULL;
+    if (ldr < N) return W8I_ESHAPE;
+    if (!aligned(residual, 2)) return W8I_EALIGN;
+    // y is the residual itself, or the two do not overlap
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(residual), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t r1 = r0 + (uintptr_t)(((int64_t)(t - 1) * ldr + N) * 2);
+    const uintptr_t y1 = y0 + (uintptr_t)(((int64_t)(t - 1) * ldy + N) * 2);
+    if (!(r0 == y0 && ldr == ldy) && r0 < y1 && y0 < r1) return W8I_ESHAPE;
+    return launch_linear_epilogue(kEpiAdd, W_q, scales, x, t, T_pad, y, N, K, ldx, ldy,
+                                  LinearEpilogue{residual, ldr, 0}, as_stream(stream));
+}
+
+int w8_linear_swiglu_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, int32_t t,
+                               int32_t T_pad, uint16_t* y, int64_t F, int64_t K, int64_t ldx, int64_t ldy,
+                               void* stream) {
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
+    if (t < 0 || t > T_pad) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (F < 1 || F > kMaxDim) return W8I_ESHAPE;
+    const int st = check_projection(W_q, scales, x, t, T_pad, y, 2 * F, K, ldx, ldy, F);
+    if (st != W8I_OK || t == 0) return st;
+    return launch_linear_epilogue(kEpiSwiGLU, W_q, scales, x, t, T_pad, y, 2 * F, K, ldx, ldy,
+                                  LinearEpilogue{nullptr, 0, F}, as_stream(stream));
 }
 
 size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) {

@@ -126,10 +126,11 @@ __device__ __forceinline__ void wait_vm() {
 
 // LS: the strip's scales are copied to LDS (when they fit beside the ring);
 // otherwise every stage loads its two scales per row with the weights.
-template <int TP16, int D, bool LS>  // TP16 = T_pad / 16 (1..4), D = ring depth in stages (2..4)
+// EPI: what is stored (see LinearEpilogue): kEpiStore, kEpiAdd or kEpiSwiGLU.
+template <int TP16, int D, bool LS, int EPI>  // TP16 = T_pad / 16 (1..4), D = ring depth in stages (2..4)
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy) {
+    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, LinearEpilogue ep) {
     static_assert(TP16 >= 1 && TP16 <= 4, "T_pad 16..64");
     static_assert(D >= 2 && D <= 4, "ring depth");
     constexpr int NT = (TP16 + 1) / 2;                // 32-column tiles
@@ -152,6 +153,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = (int)(K / kGroup);
     const int64_t n0 = (int64_t)blockIdx.x * kRows;
+    // The workgroup's 32 rows: n0 .. n0 + 31, or with the SwiGLU epilogue the
+    // 16 gate rows h0 .. h0 + 15 followed by the 16 matching up rows
+    // F + h0 .. F + h0 + 15.  Rows past the end read the last valid row (valid
+    // memory; their results are never stored).
+    const int64_t h0 = (int64_t)blockIdx.x * (kRows / 2);
+    auto row_of = [&](int rho) -> int64_t {
+        if constexpr (EPI == kEpiSwiGLU) {
+            const int64_t h = h0 + (rho & 15);
+            return (rho < 16 ? 0 : ep.F) + (h < ep.F ? h : ep.F - 1);
+        } else {
+            return n0 + rho < N ? n0 + rho : N - 1;
+        }
+    };
     const int g_begin = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave));
     const int g_end = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave + 1));
 
@@ -170,17 +184,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 
     // the strip's scales -> LDS, issued first so the wait below can leave the
     // activation ring in flight
-    const int s_loads = LS ? (64 * G + kLdsDmaBytes - 1) / kLdsDmaBytes : 0;
-    for (int k = wave; k < s_loads; k += kKSlices)
+    // (SwiGLU: the gate rows' and the up rows' scales are two blocks of 32 G
+    // bytes, each copied to its own LDS region of whole 1 KB pieces)
+    const int s_block = LS ? (EPI == kEpiSwiGLU ? 32 * G : 64 * G) : 0;
+    const int s_pieces = (s_block + kLdsDmaBytes - 1) / kLdsDmaBytes;
+    const int s_loads = EPI == kEpiSwiGLU ? 2 * s_pieces : s_pieces;
+    for (int k = wave; k < s_loads; k += kKSlices) {
+        const int blk = EPI == kEpiSwiGLU && k >= s_pieces ? 1 : 0;
+        const int piece = k - blk * s_pieces;
+        const int64_t first_row = EPI == kEpiSwiGLU ? blk * ep.F + h0 : n0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, W8I_LDS(s_raw + k * kLdsDmaBytes), 16, 16u * lane,
-                                                 (uint32_t)(n0 * G * 2) + (uint32_t)(k * kLdsDmaBytes), 0, 0);
+                                                 (uint32_t)(first_row * G * 2) + (uint32_t)(piece * kLdsDmaBytes),
+                                                 0, 0);
+    }
 
     uint32_t w_off[2];     // this lane's weight piece in group 0 of the stage
     uint32_t w_off_gs[2];  // ... in the group it carries, (lane >> 4) & 1
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int64_t nr = n0 + 16 * i + (lane & 15);
-        w_off[i] = (uint32_t)((nr < N ? nr : N - 1) * K) + 16u * (lane >> 5);
+        w_off[i] = (uint32_t)(row_of(16 * i + (lane & 15)) * K) + 16u * (lane >> 5);
         w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
     }
     // direct load i of a stage: columns 8 i .. 8 i + 7 (sized for two tiles: an
@@ -226,8 +248,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t s_none =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(S), (short)0, 0, 0x00020000);
-    // this lane's row of scales (per-stage scale loads)
-    const uint32_t s_row_off = (uint32_t)((n0 + r < N ? n0 + r : N - 1) * G) * 2u;
+    // this lane's row of scales (per-stage scale loads), and its place in LDS
+    const uint32_t s_row_off = (uint32_t)(row_of(r) * G) * 2u;
+    const int s_row_lds = EPI == kEpiSwiGLU ? (r >> 4) * (s_pieces * kLdsDmaBytes / 2) + (r & 15) * G : r * G;
 
     auto slot = [&](int u) -> unsigned char* { return u == 0 ? xr0 : u == 1 ? xr1 : u == 2 ? xr2 : xr3; };
     // stage starting at group g; `single` loads group g alone in position 0
@@ -254,7 +277,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     auto step = [&](const u32x4 (&w)[2], const uint16_t (&ss)[2], const unsigned char* xs, int gs, int g) {
         const bf16x8 b_lo = dequant8(w[gs].x, w[gs].y);
         const bf16x8 b_hi = dequant8(w[gs].z, w[gs].w);
-        const uint16_t s16 = LS ? s_lds[r * G + g] : ss[gs];
+        const uint16_t s16 = LS ? s_lds[s_row_lds + g] : ss[gs];
         const double sc = (double)(float)__builtin_bit_cast(_Float16, s16);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -371,7 +394,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
         // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns) of tile tt
         const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
-        if (n < N && j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(sum);
+        const uint16_t b = f64_to_bf16(sum);
+        if constexpr (EPI == kEpiSwiGLU) {
+            // lane r < 16 holds gate row h0 + r, lane r + 16 the up row of the
+            // same h, both for column j
+            const uint16_t up = (uint16_t)__shfl_xor((int)b, 16);
+            const int64_t h = h0 + r;
+            if (r < 16 && h < ep.F && j < t) Y[(int64_t)j * ldy + h] = swiglu_bf16(b, up);
+        } else if constexpr (EPI == kEpiAdd) {
+            // the residual element is read before its own output is written
+            // (y may be the residual itself)
+            if (n < N && j < t) Y[(int64_t)j * ldy + n] = add_bf16(b, ep.r[(int64_t)j * ep.ldr + n]);
+        } else {
+            if (n < N && j < t) Y[(int64_t)j * ldy + n] = b;
+        }
     }
 }
 
@@ -662,38 +698,54 @@ struct LinearPlan {
                       // tiles kernel: whether it loads the scales by blocks
 };
 
-static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
-    const int tp16 = T_pad / 16;
-    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) {
-        const bool sc = (K / kGroup) % 8 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
-        return {LinearKernel::kTiles, tp16, 0, sc};
-    }
-    // the LDS-staged variant: with the deepest ring (3 or 2 stages for one
-    // 32-column tile, 2 for two) whose LDS leaves room for the strip's scales
-    // when they can be copied as 16-byte pieces (scales 16-byte aligned);
-    // otherwise with the deepest ring and the scales loaded per stage.  (A
-    // depth of 3 measured faster than 4 at T_pad: more loads in flight only
-    // queue longer.)
-    const int64_t s_bytes = (64 * (K / kGroup) + kLdsDmaBytes - 1) / kLdsDmaBytes * kLdsDmaBytes;
+// The LDS-staged variant: the deepest ring (3 or 2 stages for one 32-column
+// tile, 2 for two) whose LDS leaves room for the strip's scales when they can
+// be copied as 16-byte pieces (s_bytes: the scale bytes the strip needs in
+// LDS, 0 when they cannot be copied); otherwise the deepest ring with the
+// scales loaded per stage.  (A depth of 3 measured faster than 4 at T_pad:
+// more loads in flight only queue longer.)
+static LinearPlan plan_split(int tp16, int64_t s_bytes) {
     const int nt = (tp16 + 1) / 2;
     const int dmax = nt == 1 ? 3 : 2;
-    if ((reinterpret_cast<uintptr_t>(S) & 15) == 0) {
+    if (s_bytes > 0) {
         for (int D = dmax; D >= 2; --D)
             if (s_bytes <= split_lds_scale_bytes(nt, D)) return {LinearKernel::kSplitLds, tp16, D, true};
     }
     return {LinearKernel::kSplitLds, tp16, dmax, false};
 }
 
+static int64_t round_dma(int64_t bytes) { return (bytes + kLdsDmaBytes - 1) / kLdsDmaBytes * kLdsDmaBytes; }
+
+static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
+    const int tp16 = T_pad / 16;
+    const bool s16 = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) {
+        const bool sc = (K / kGroup) % 8 == 0 && s16;
+        return {LinearKernel::kTiles, tp16, 0, sc};
+    }
+    return plan_split(tp16, s16 ? round_dma(64 * (K / kGroup)) : 0);
+}
+
+// SwiGLU rows: two scale blocks of 32 G bytes; the up rows' block starts at
+// byte 2 F G, which the 16-byte pieces need 16-byte aligned
+static LinearPlan plan_epilogue(int epi, int64_t N, int64_t K, int T_pad, const void* S) {
+    const int64_t G = K / kGroup;
+    const bool s16 = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+    if (epi == kEpiSwiGLU) return plan_split(T_pad / 16, s16 && ((N / 2) * G) % 8 == 0 ? 2 * round_dma(32 * G) : 0);
+    return plan_split(T_pad / 16, s16 ? round_dma(64 * G) : 0);
+}
+
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     static const char* const tiles[2][2] = {{"gemm_w8g32_tiles<1, false>", "gemm_w8g32_tiles<1, true>"},
                                             {"gemm_w8g32_tiles<2, false>", "gemm_w8g32_tiles<2, true>"}};
     static const char* const split_lds[4][3] = {
-        {"gemm_w8g32_split_lds<1, 2, true>", "gemm_w8g32_split_lds<1, 3, true>", ""},
-        {"gemm_w8g32_split_lds<2, 2, true>", "gemm_w8g32_split_lds<2, 3, true>", ""},
-        {"gemm_w8g32_split_lds<3, 2, true>", "", ""},
-        {"gemm_w8g32_split_lds<4, 2, true>", "", ""}};
-    static const char* const split_lds_gs[4] = {"gemm_w8g32_split_lds<1, 3, false>", "gemm_w8g32_split_lds<2, 3, false>",
-                                                "gemm_w8g32_split_lds<3, 2, false>", "gemm_w8g32_split_lds<4, 2, false>"};
+        {"gemm_w8g32_split_lds<1, 2, true, 0>", "gemm_w8g32_split_lds<1, 3, true, 0>", ""},
+        {"gemm_w8g32_split_lds<2, 2, true, 0>", "gemm_w8g32_split_lds<2, 3, true, 0>", ""},
+        {"gemm_w8g32_split_lds<3, 2, true, 0>", "", ""},
+        {"gemm_w8g32_split_lds<4, 2, true, 0>", "", ""}};
+    static const char* const split_lds_gs[4] = {
+        "gemm_w8g32_split_lds<1, 3, false, 0>", "gemm_w8g32_split_lds<2, 3, false, 0>",
+        "gemm_w8g32_split_lds<3, 2, false, 0>", "gemm_w8g32_split_lds<4, 2, false, 0>"};
     if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
     const LinearPlan p = plan_linear(N, K, T_pad, S);
     switch (p.kind) {
@@ -704,41 +756,58 @@ const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     }
 }
 
+template <int EPI>
+static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
+                        uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+                        hipStream_t stream) {
+    const int64_t wgs = EPI == kEpiSwiGLU ? (ep.F + kRows / 2 - 1) / (kRows / 2) : (N + kRows - 1) / kRows;
+    const dim3 grid((unsigned)wgs);
+    const dim3 block(kGemmThreads);
+#define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                     \
+    case TP * 16 + D * 2 + LS:                                                                          \
+        hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D, LS, EPI>), grid, block, 0, stream, W, S, X, Y, N, K, t, \
+                           ldx, ldy, ep);                                                               \
+        break;
+    switch (p.tp16 * 16 + p.depth * 2 + (p.lds_scales ? 1 : 0)) {
+        W8I_SPLIT_LAUNCH(1, 2, true)
+        W8I_SPLIT_LAUNCH(1, 3, true)
+        W8I_SPLIT_LAUNCH(2, 2, true)
+        W8I_SPLIT_LAUNCH(2, 3, true)
+        W8I_SPLIT_LAUNCH(3, 2, true)
+        W8I_SPLIT_LAUNCH(4, 2, true)
+        W8I_SPLIT_LAUNCH(1, 3, false)
+        W8I_SPLIT_LAUNCH(2, 3, false)
+        W8I_SPLIT_LAUNCH(3, 2, false)
+        W8I_SPLIT_LAUNCH(4, 2, false)
+        default:
+            return W8I_ET;
+    }
+#undef W8I_SPLIT_LAUNCH
+    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+}
+
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                   int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
     const LinearPlan p = plan_linear(N, K, T_pad, S);
-    const dim3 grid((unsigned)((N + kRows - 1) / kRows));
-    const dim3 block(kGemmThreads);
     switch (p.kind) {
         case LinearKernel::kTiles:
             return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, p.lds_scales, stream);
-        case LinearKernel::kSplitLds: {
-#define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                  \
-    case TP * 16 + D * 2 + LS:                                                                       \
-        hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D, LS>), grid, block, 0, stream, W, S, X, Y, N, K, t, \
-                           ldx, ldy);                                                                \
-        break;
-            switch (p.tp16 * 16 + p.depth * 2 + (p.lds_scales ? 1 : 0)) {
-                W8I_SPLIT_LAUNCH(1, 2, true)
-                W8I_SPLIT_LAUNCH(1, 3, true)
-                W8I_SPLIT_LAUNCH(2, 2, true)
-                W8I_SPLIT_LAUNCH(2, 3, true)
-                W8I_SPLIT_LAUNCH(3, 2, true)
-                W8I_SPLIT_LAUNCH(4, 2, true)
-                W8I_SPLIT_LAUNCH(1, 3, false)
-                W8I_SPLIT_LAUNCH(2, 3, false)
-                W8I_SPLIT_LAUNCH(3, 2, false)
-                W8I_SPLIT_LAUNCH(4, 2, false)
-                default:
-                    return W8I_ET;
-            }
-#undef W8I_SPLIT_LAUNCH
-            break;
-        }
+        case LinearKernel::kSplitLds:
+            return launch_split<kEpiStore>(p, W, S, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
         default:
             return W8I_ESHAPE;
     }
-    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+}
+
+int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
+                           uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+                           hipStream_t stream) {
+    const LinearPlan p = plan_epilogue(epi, N, K, T_pad, S);
+    switch (epi) {
+        case kEpiAdd: return launch_split<kEpiAdd>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+        case kEpiSwiGLU: return launch_split<kEpiSwiGLU>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+        default: return W8I_ESHAPE;
+    }
 }
 
 }  // namespace w8i

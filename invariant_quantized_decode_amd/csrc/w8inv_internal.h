@@ -20,8 +20,23 @@ __host__ __device__ __forceinline__ int64_t kslice_begin(int64_t G, int i) {
     return i >= kKSlices ? G : 2 * (((G / 2) * i) / kKSlices);
 }
 
+// What the projection kernel stores for output (j, n).
+constexpr int kEpiStore = 0;   // y = bf16(W x)
+constexpr int kEpiAdd = 1;     // y = residual add of bf16(W x) and r (the glue's w8i_residual_add)
+constexpr int kEpiSwiGLU = 2;  // rows [0, F) gate, [F, 2F) up; y[:, h] = SwiGLU(gate h, up h) (w8i_swiglu)
+struct LinearEpilogue {
+    const uint16_t* r;  // kEpiAdd: residual, bf16 [t, ldr]
+    int64_t ldr;
+    int64_t F;          // kEpiSwiGLU: gate rows (the projection has 2F rows)
+};
+
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                   int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+// the projection with a fused epilogue (always the LDS-staged split kernel);
+// for kEpiSwiGLU, N is the projection's 2F rows and y has F columns
+int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
+                           uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+                           hipStream_t stream);
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S);
 
 size_t logprob_workspace_bytes(int t, int64_t V, int block);

@@ -54,6 +54,27 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
     return f32_to_bf16(__uint_as_float(u));
 }
 
+// ------------------------------------------------------------ layer glue
+// The column-local glue between the projections of one decode layer.  The
+// glue kernels and the fused projection epilogues both call these, so a fused
+// epilogue gives the bits of the projection followed by the glue kernel.
+
+// residual add: fp32 sum of two bf16 values, rounded to bf16 nearest-even
+__device__ __forceinline__ uint16_t add_bf16(uint16_t a, uint16_t b) {
+    return f32_to_bf16(bf16_to_f32(a) + bf16_to_f32(b));
+}
+
+// SwiGLU: silu(g) * u = g / (1 + e^-g) * u in fp64, rounded once to bf16.  In
+// fp64, e^-g of any bf16 gate is finite or its silu is below bf16's range, so
+// the final rounding is the only one that matters (in fp32, e^-g overflows
+// for g < -88.7 while g e^g u can still be a normal bf16).
+__device__ __forceinline__ uint16_t swiglu_bf16(uint16_t gate, uint16_t up) {
+    const double g = (double)bf16_to_f32(gate);
+    const double u = (double)bf16_to_f32(up);
+    const double silu = g / (1.0 + ::exp(-g));
+    return f64_to_bf16(silu * u);
+}
+
 // ------------------------------------------------------------ double-double
 
 struct dd {

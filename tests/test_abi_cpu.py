@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -30,13 +30,13 @@ def test_every_declared_symbol_is_exported():
 def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
     """The kernel-name query is host-only; it names one kernel per (N, K, T_pad, scales alignment)."""
     q = L.w8_linear_invariant_kernel
-    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true>"
-    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false>"  # scales not 16-byte aligned
+    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true, 0>"
+    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false, 0>"  # scales not 16-byte aligned
     assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2, true>"
     assert q(248320, 5120, 32, fake(4098)) == b"gemm_w8g32_tiles<2, false>"   # scales not 16-byte aligned
     assert q(248320, 5088, 16, fake(4096)) == b"gemm_w8g32_tiles<1, false>"   # K/32 = 159
-    assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true>"
-    assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false>"  # scales too large for LDS
+    assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true, 0>"
+    assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false, 0>"  # scales too large for LDS
     for bad in ((6144, 5100, 32), (0, 5120, 32), (6144, 5120, 24), (6144, 5120, 80)):
         assert q(*bad, fake(4096)) == b""
 
@@ -74,6 +74,40 @@ def test_linear_rejects_invalid_arguments(kw, code):
 def test_linear_t_zero_is_a_no_op():
     assert linear(t=0, W=0, S=0, X=0, Y=0) == 0
     assert L.w8_linear_invariant_workspace_bytes(6144, 5120, 32) == 0
+
+
+def linear_add(W=A, S=A, X=A, R=A + 0x100000, t=4, T=32, Y=A + 0x200000, N=64, K=256, ldx=256, ldr=64, ldy=64):
+    return L.w8_linear_add_invariant(fake(W) if W else None, fake(S) if S else None, fake(X) if X else None,
+                                     fake(R) if R else None, t, T, fake(Y) if Y else None, N, K, ldx, ldr, ldy, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=24), -4), (dict(t=33), -4), (dict(R=0), -1), (dict(W=0), -1), (dict(ldr=32), -2),
+    (dict(R=A + 0x100001), -3), (dict(X=A + 4), -3), (dict(K=100, ldx=100), -2),
+    (dict(R=A + 0x200000 + 2), -2),                    # residual overlaps y without being y
+    (dict(R=A + 0x200000, ldr=128, ldy=64), -2),       # same pointer, different strides
+])
+def test_linear_add_rejects_invalid_arguments(kw, code):
+    assert linear_add(**kw) == code
+
+
+def test_linear_add_accepts_y_equal_to_residual_and_t_zero():
+    assert linear_add(t=0, W=0, S=0, X=0, R=0, Y=0) == 0
+    # validation passes for exact aliasing (launch not reached: t = 0 short-circuits before any device work)
+    assert linear_add(t=0, R=A + 0x200000) == 0
+
+
+def linear_swiglu(W=A, S=A, X=A, t=4, T=32, Y=A, F=64, K=256, ldx=256, ldy=64):
+    return L.w8_linear_swiglu_invariant(fake(W) if W else None, fake(S) if S else None, fake(X) if X else None,
+                                        t, T, fake(Y) if Y else None, F, K, ldx, ldy, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=80), -4), (dict(t=-1), -4), (dict(F=0), -2), (dict(ldy=63), -2), (dict(Y=0), -1), (dict(S=0), -1),
+    (dict(W=A + 4), -3), (dict(K=96, ldx=96, F=1 << 31), -2),   # 2F * K >= 2^32
+])
+def test_linear_swiglu_rejects_invalid_arguments(kw, code):
+    assert linear_swiglu(**kw) == code
 
 
 def logprob(Lg=A, T=A, block=4096, out=A, t=4, V=248320, ldl=248320, ws=A, wsb=1 << 20):

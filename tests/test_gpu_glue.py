@@ -31,7 +31,7 @@ def check(y_bits, ref, label, ulps=1.0):
 
 
 @pytest.mark.parametrize("t,H,weighted", [(7, 5120, False), (32, 5120, True), (3, 1000, True), (2, 65536, False),
-                                          (5, 1, False), (1, 17, True)])
+                                          (5, 1, False), (1, 17, True), (4, 4100, True), (3, 12288, True)])
 def test_rmsnorm_matches_oracle(t, H, weighted):
     say(f"case rmsnorm t={t} H={H} weighted={weighted}")
     rng = np.random.default_rng(t * 1000 + H)
@@ -55,6 +55,14 @@ def test_rmsnorm_columns_are_independent_and_strided_rows_identical():
     out = torch.zeros((t, H + 24), dtype=torch.bfloat16, device=DEV)
     w8.w8i_rmsnorm(wide[:, 8:8 + H], 1e-6, y=out[:, :H])
     assert np.array_equal(bits(out[:, :H]), base)
+    # rows and outputs off 16-byte alignment take the 2-byte loads and stores
+    for xo, yo in ((1, 0), (8, 3), (3, 5)):
+        say(f"case rmsnorm offsets x+{xo} y+{yo}")
+        wide.zero_()
+        wide[:, xo:xo + H] = bf16(x)
+        out.zero_()
+        w8.w8i_rmsnorm(wide[:, xo:xo + H], 1e-6, y=out[:, yo:yo + H])
+        assert np.array_equal(bits(out[:, yo:yo + H]), base)
 
 
 def test_rmsnorm_zero_column_and_large_values():
