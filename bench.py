@@ -233,30 +233,43 @@ def run_all(torch, w8, synth, dev, args):
 
     chain = [("chain qkv 7168x5120", 7168, 5120), ("chain o 5120x6144", 5120, 6144),
              ("chain gate+up 34816x5120", 34816, 5120), ("chain down 5120x17408", 5120, 17408)]
-    work = [(c.name, c.N, c.K, c.T_pad, c.scale_eps) for c in
+    work = [(c.name, c.N, c.K, c.T_pad, c.scale_eps, "linear") for c in
             (synth.LINEAR_1024, synth.LINEAR_6144, synth.MLP_GATE_UP, synth.MLP_DOWN, synth.HEAD)]
-    work += [(n, N, K, synth.CHAIN_T_PAD, 0.0) for n, N, K in chain]
+    work += [(n, N, K, synth.CHAIN_T_PAD, 0.0, "linear") for n, N, K in chain]
+    # the chain's projections with their glue fused into the epilogue
+    work += [("chain o + residual (fused) 5120x6144", 5120, 6144, synth.CHAIN_T_PAD, 0.0, "add"),
+             ("chain gate+up + SwiGLU (fused) 34816x5120", 34816, 5120, synth.CHAIN_T_PAD, 0.0, "swiglu"),
+             ("chain down + residual (fused) 5120x17408", 5120, 17408, synth.CHAIN_T_PAD, 0.0, "add")]
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     stream = torch.cuda.Stream(device=dev)
-    for name, N, K, T_pad, eps in work:
+    for name, N, K, T_pad, eps, op in work:
         wbytes = N * K + 2 * N * (K // 32)
         copies = max(1, math.ceil((1 << 30) / wbytes))
         Ws = [torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8, device=dev) for _ in range(copies)]
         Ss = [(torch.randn(N, K // 32, generator=g, device=dev).abs_() * 0.02 + eps).half() for _ in range(copies)]
         X = torch.randn(T_pad, K, generator=g, device=dev).to(torch.bfloat16)
-        Y = torch.empty((T_pad, N), dtype=torch.bfloat16, device=dev)
-        kernel = w8.w8_linear_invariant_kernel(N, K, T_pad, Ss[0])
+        R = torch.randn(T_pad, N, generator=g, device=dev).to(torch.bfloat16)
+        Y = torch.empty((T_pad, N // 2 if op == "swiglu" else N), dtype=torch.bfloat16, device=dev)
+        if op == "linear":
+            kernel = w8.w8_linear_invariant_kernel(N, K, T_pad, Ss[0])
+            call = lambda i, t: w8.w8_linear_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)  # noqa: E731
+        elif op == "add":
+            kernel = "gemm_w8g32_split_lds, residual-add epilogue"
+            call = lambda i, t: w8.w8_linear_add_invariant(Ws[i], Ss[i], X[:t], R[:t], t, T_pad, y=Y)  # noqa: E731
+        else:
+            kernel = "gemm_w8g32_split_lds, SwiGLU epilogue"
+            call = lambda i, t: w8.w8_linear_swiglu_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)  # noqa: E731
         for t in (1, T_pad):
             reps = max(2, math.ceil(20000 / copies))  # about 20000 launches, fewer for the largest
             reps = min(reps, max(2, int(2e10 // (wbytes * copies))))
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.stream(stream):
-                w8.w8_linear_invariant(Ws[0], Ss[0], X[:t], t, T_pad, y=Y)
+                call(0, t)
                 torch.cuda.synchronize()
                 with torch.cuda.graph(graph, stream=stream):
                     for i in range(copies):
-                        w8.w8_linear_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)
+                        call(i, t)
                 graph.replay()
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -266,7 +279,8 @@ def run_all(torch, w8, synth, dev, args):
                 e1.record(stream)
                 torch.cuda.synchronize()
             sec = e0.elapsed_time(e1) / 1e3 / (reps * copies)
-            alg = wbytes + 2 * t * (K + N)
+            # algorithmic bytes: weights and scales, x, y (and the residual read)
+            alg = wbytes + 2 * t * K + 2 * t * Y.shape[1] + (2 * t * N if op == "add" else 0)
             # CPU oracle on a 64-row sample of the same projection
             rows = np.arange(0, N, max(1, N // 64))[:64]
             qh = Ws[0][rows].cpu().numpy()
