@@ -104,6 +104,43 @@ int w8_linear_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_
 const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t *scales);
 
 /* ---------------------------------------------------------------------------
+ * Packed weight layout (optional).
+ *
+ * The same W8G32 projection over weights rearranged once, at load time, into
+ * the order the projection kernel streams them: per 32-row strip and pair of
+ * groups, one 2 KB block of codes already in the matrix-core operand order
+ * (whole cache lines per load, no register shuffles) and one 128-byte line of
+ * its 64 scales (no staging of scales before the main loop).  Only the layout
+ * changes: w8_linear_invariant_packed(w8_pack(W_q, scales), ...) gives the bits
+ * of w8_linear_invariant(W_q, scales, ...) for every argument, with the same K
+ * plan.  (Source of the operation: as for w8_linear_invariant.)
+ *
+ * Layout, with G = K/32, P = ceil(G/2) and strips = ceil(N/32):
+ *   Wp int8 [strips][P][2048]: byte 1024 gs + 512 c + 16 r + b of block (s, p)
+ *      is W_q[32 s + r][64 p + 32 gs + 16 c + b]   (r < 32; gs, c < 2; b < 16)
+ *   Sp fp16 [strips][P][64]:   element 2 r + gs of block (s, p) is
+ *      scales[32 s + r][2 p + gs]
+ *   Rows past N, and the group past an odd G, are zero.
+ *
+ * w8_pack_bytes: the sizes of Wp and Sp (W8I_ESHAPE when Wp would reach 4 GiB).
+ * w8_pack: writes Wp and Sp (device buffers of those sizes, 16-byte aligned)
+ *   from W_q (16-byte aligned) and scales (2-byte aligned) on `stream`; no
+ *   overlap between the inputs and the outputs.
+ * w8_linear_invariant_packed: as w8_linear_invariant (x, y, t, T_pad, N, K,
+ *   ldx, ldy and their rules), with Wp / Sp from w8_pack(N, K) (16-byte
+ *   aligned).  No workspace.  Any N (one kernel family: the LDS-staged split
+ *   kernel with per-stage scale loads).
+ * ------------------------------------------------------------------------- */
+int w8_pack_bytes(int64_t N, int64_t K, size_t *wp_bytes, size_t *sp_bytes);
+
+int w8_pack(const int8_t *W_q, const uint16_t *scales, int64_t N, int64_t K, int8_t *Wp, uint16_t *Sp,
+            void *stream);
+
+int w8_linear_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint16_t *x, int32_t t,
+                               int32_t T_pad, uint16_t *y, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
+                               void *stream);
+
+/* ---------------------------------------------------------------------------
  * Fused W8 projection epilogues.
  *
  * Source: the ninfer issue (GitHub issue 80), table "Where t selects

@@ -26,6 +26,7 @@ STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: 
 
 EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
            "w8_linear_invariant_kernel", "w8_linear_add_invariant", "w8_linear_swiglu_invariant",
+           "w8_pack_bytes", "w8_pack", "w8_linear_invariant_packed",
            "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32")
 
@@ -50,6 +51,9 @@ def _load():
     L.w8_linear_invariant_kernel.argtypes, L.w8_linear_invariant_kernel.restype = [I64, I64, I32, P], ctypes.c_char_p
     L.w8_linear_add_invariant.argtypes = [P, P, P, P, I32, I32, P, I64, I64, I64, I64, I64, P]
     L.w8_linear_swiglu_invariant.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
+    L.w8_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    L.w8_pack.argtypes = [P, P, I64, I64, P, P, P]
+    L.w8_linear_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
     L.vocab_block_logprob_workspace_bytes.argtypes = [I32, I64, I32]
     L.vocab_block_logprob_workspace_bytes.restype = SZ
     L.vocab_block_logprob.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
@@ -59,7 +63,8 @@ def _load():
     L.w8i_residual_add.argtypes = [P, P, P, I32, I64, I64, I64, I64, P]
     L.w8i_exp32.argtypes = [P, P, I64, P]
     L.w8i_log32.argtypes = [P, P, I64, P]
-    for name in ("w8_linear_add_invariant", "w8_linear_swiglu_invariant", "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
+    for name in ("w8_linear_add_invariant", "w8_linear_swiglu_invariant", "w8_pack_bytes", "w8_pack",
+                 "w8_linear_invariant_packed", "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -170,6 +175,53 @@ def w8_linear_swiglu_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch
     st = _lib.w8_linear_swiglu_invariant(_ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y), F, K, ldx,
                                          ldy, ctypes.c_void_p(_stream(W_q.device)))
     _check("w8_linear_swiglu_invariant", st)
+    return y
+
+
+def w8_pack_bytes(N: int, K: int) -> tuple[int, int]:
+    """(codes bytes, scale bytes) of the packed layout of an [N, K] projection."""
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("w8_pack_bytes", _lib.w8_pack_bytes(int(N), int(K), ctypes.byref(wb), ctypes.byref(sb)))
+    return wb.value, sb.value
+
+
+def w8_pack(W_q: torch.Tensor, scales: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """The packed layout (Wp int8, Sp fp16-as-int16) of W_q int8 [N, K] and scales fp16 [N, K/32]."""
+    if W_q.dtype != torch.int8 or W_q.dim() != 2 or not W_q.is_contiguous():
+        raise ValueError("W_q must be a contiguous int8 [N, K] tensor")
+    N, K = W_q.shape
+    if scales.dtype not in (torch.float16, torch.int16) or tuple(scales.shape) != (N, K // 32) \
+            or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp16 [N, K/32] tensor")
+    _same_gpu(("W_q", W_q), ("scales", scales))
+    wb, sb = w8_pack_bytes(N, K)
+    Wp = torch.empty(wb, dtype=torch.int8, device=W_q.device)
+    Sp = torch.empty(sb // 2, dtype=torch.int16, device=W_q.device)
+    _check("w8_pack", _lib.w8_pack(_ptr(W_q), _ptr(scales), N, K, _ptr(Wp), _ptr(Sp),
+                                   ctypes.c_void_p(_stream(W_q.device))))
+    return Wp, Sp
+
+
+def w8_linear_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, t: int, T_pad: int, N: int,
+                               y: torch.Tensor | None = None) -> torch.Tensor:
+    """w8_linear_invariant over the packed layout from w8_pack (same bits).  x bf16 [>=t, K]; y bf16 [t, N]."""
+    K = x.size(1)
+    wb, sb = w8_pack_bytes(N, K)
+    if Wp.dtype != torch.int8 or Wp.numel() != wb or not Wp.is_contiguous():
+        raise ValueError("Wp must be the contiguous int8 output of w8_pack for this N and K")
+    if Sp.dtype not in (torch.int16, torch.float16) or Sp.numel() * 2 != sb or not Sp.is_contiguous():
+        raise ValueError("Sp must be the contiguous output of w8_pack for this N and K")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.size(0) < t:
+        raise ValueError("x must be a bf16 [>=t, K] tensor")
+    if y is None:
+        y = torch.empty((t, N), dtype=torch.bfloat16, device=Wp.device)
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != N or y.size(0) < t:
+        raise ValueError("y must be a bf16 [>=t, N] tensor")
+    _same_gpu(("Wp", Wp), ("Sp", Sp), ("x", x), ("y", y))
+    st = _lib.w8_linear_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y), int(N), K,
+                                         _row_major(x, "x"), _row_major(y, "y"),
+                                         ctypes.c_void_p(_stream(Wp.device)))
+    _check("w8_linear_invariant_packed", st)
     return y
 
 

@@ -76,6 +76,32 @@ const char* w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, cons
     return linear_kernel_name(N, K, T_pad, scales);
 }
 
+int w8_pack_bytes(int64_t N, int64_t K, size_t* wp_bytes, size_t* sp_bytes) {
+    if (!wp_bytes || !sp_bytes) return W8I_ENULL;
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return W8I_ESHAPE;
+    if (packed_weight_bytes(N, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    *wp_bytes = (size_t)packed_weight_bytes(N, K);
+    *sp_bytes = (size_t)packed_scale_bytes(N, K);
+    return W8I_OK;
+}
+
+int w8_pack(const int8_t* W_q, const uint16_t* scales, int64_t N, int64_t K, int8_t* Wp, uint16_t* Sp, void* stream) {
+    if (!W_q || !scales || !Wp || !Sp) return W8I_ENULL;
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return W8I_ESHAPE;
+    if (packed_weight_bytes(N, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (!aligned(W_q, 16) || !aligned(scales, 2) || !aligned(Wp, 16) || !aligned(Sp, 16)) return W8I_EALIGN;
+    return launch_pack(W_q, scales, N, K, Wp, Sp, as_stream(stream));
+}
+
+int w8_linear_invariant_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* x, int32_t t, int32_t T_pad,
+                               uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream) {
+    const int st = check_projection(Wp, Sp, x, t, T_pad, y, N, K, ldx, ldy, N);
+    if (st != W8I_OK || t == 0) return st;
+    if (packed_weight_bytes(N, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (!aligned(Sp, 16)) return W8I_EALIGN;
+    return launch_linear_packed(Wp, Sp, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
+}
+
 int w8_linear_add_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const uint16_t* residual,
                             int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldr,
                             int64_t ldy, void* stream) {

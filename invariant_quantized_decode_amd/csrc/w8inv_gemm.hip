@@ -127,7 +127,10 @@ __device__ __forceinline__ void wait_vm() {
 // LS: the strip's scales are copied to LDS (when they fit beside the ring);
 // otherwise every stage loads its two scales per row with the weights.
 // EPI: what is stored (see LinearEpilogue): kEpiStore, kEpiAdd or kEpiSwiGLU.
-template <int TP16, int D, bool LS, int EPI>  // TP16 = T_pad / 16 (1..4), D = ring depth in stages (2..4)
+// PK: W and S are in the packed layout (w8_pack): each stage's weights are two
+// contiguous 1 KB blocks already in the matrix-core lane order, and its scales
+// one 128-byte line, loaded with the stage.
+template <int TP16, int D, bool LS, int EPI, bool PK>  // TP16 = T_pad / 16 (1..4), D = ring depth (2..4)
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, LinearEpilogue ep) {
@@ -139,7 +142,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     constexpr int kSlotBytes = split_lds_slot_bytes(NT);
     constexpr int kScaleBytes = LS ? split_lds_scale_bytes(NT, D) : 16;
     constexpr int kXLoads = 4 * NT;                   // direct loads of 8 columns x 128 bytes per stage
-    constexpr int kLoadsPerStage = 2 + kXLoads + (LS ? 0 : 2);  // weights + activations (+ scales)
+    // weights + activations (+ scales)
+    constexpr int kLoadsPerStage = 2 + kXLoads + (PK ? 1 : LS ? 0 : 2);
+    static_assert(!PK || (!LS && EPI == kEpiStore), "packed layout: scales per stage, plain store");
     static_assert(kScaleBytes > 0, "LDS");
     // one array per ring slot, so the compiler can wait for each slot's loads alone
     __shared__ __align__(16) unsigned char xr0[kSlotBytes];
@@ -171,8 +176,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 
     // Rows past N read row N-1 and columns past t read column t-1 (valid
     // memory, results never stored); the descriptors' ranges bound every access.
-    const __amdgpu_buffer_rsrc_t w_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(N * K), 0x00020000);
+    // packed layout: whole strips of P = ceil(G/2) stage blocks (2 KB of codes, 128 bytes of scales)
+    const int64_t P = (G + 1) / 2;
+    const int64_t strips = (N + kRows - 1) / kRows;
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(PK ? strips * P * 2048 : N * K), 0x00020000);
     const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
     // The range is rounded up to whole 16-byte pieces: a piece that straddles
@@ -180,7 +188,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     // included.  S is 16-byte aligned here, so the rounded piece lies in the
     // same aligned 16 bytes (and page) as the last scales.
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S), (short)0, (int)(((uint32_t)(N * G * 2) + 15u) & ~15u), 0x00020000);
+        const_cast<uint16_t*>(S), (short)0,
+        (int)(PK ? (uint32_t)(strips * P * 128) : ((uint32_t)(N * G * 2) + 15u) & ~15u), 0x00020000);
 
     // the strip's scales -> LDS, issued first so the wait below can leave the
     // activation ring in flight
@@ -205,6 +214,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         w_off[i] = (uint32_t)(row_of(16 * i + (lane & 15)) * K) + 16u * (lane >> 5);
         w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
     }
+    // packed: lane l takes bytes 16 l .. 16 l + 15 of each 1 KB block (row l % 32,
+    // K half l / 32 of the block's group) and the 4 bytes of its row's two scales
+    const uint32_t pk_w = (uint32_t)(blockIdx.x * P * 2048) + 16u * lane;
+    const uint32_t pk_s = (uint32_t)(blockIdx.x * P * 128) + 4u * (lane & 31);
     // direct load i of a stage: columns 8 i .. 8 i + 7 (sized for two tiles: an
     // array whose size depends on the template arguments, captured by the
     // lambdas below, made the host pass drop the kernel stubs)
@@ -255,29 +268,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     auto slot = [&](int u) -> unsigned char* { return u == 0 ? xr0 : u == 1 ? xr1 : u == 2 ? xr2 : xr3; };
     // stage starting at group g; `single` loads group g alone in position 0
     // (the odd last group)
-    auto load_stage = [&](int g, u32x4 (&w)[2], uint16_t (&sc)[2], unsigned char* xs, bool single) {
+    // (packed: the stage block of group g, both groups, and its scale line)
+    auto load_stage = [&](int g, u32x4 (&w)[2], uint16_t (&sc)[2], uint32_t& sp, unsigned char* xs, bool single) {
         const bool live = single || g <= last_full;
         const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
         const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
-        if constexpr (!LS) {
+        if constexpr (PK) {
+            const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
+            sp = __builtin_amdgcn_raw_buffer_load_b32(sr, pk_s, g * 64, 0);
+        } else if constexpr (!LS) {
             const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
             sc[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * g, 0, 0);
             sc[1] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * (single ? g : g + 1), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
+            w[i] = __builtin_bit_cast(
+                u32x4, PK ? __builtin_amdgcn_raw_buffer_load_b128(wr, pk_w + 1024u * i, g * 1024, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b128(wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, W8I_LDS(xs + wave * kStageBytes + i * kLdsDmaBytes), 16,
                                                      xd_off[i], g * (2 * kGroup), 0, 0);
     };
     // group gs of the stage (weights already swapped), acc += s * D_g in fp64
-    auto step = [&](const u32x4 (&w)[2], const uint16_t (&ss)[2], const unsigned char* xs, int gs, int g) {
+    auto step = [&](const u32x4 (&w)[2], const uint16_t (&ss)[2], uint32_t sp, const unsigned char* xs, int gs,
+                    int g) {
         const bf16x8 b_lo = dequant8(w[gs].x, w[gs].y);
         const bf16x8 b_hi = dequant8(w[gs].z, w[gs].w);
-        const uint16_t s16 = LS ? s_lds[s_row_lds + g] : ss[gs];
+        const uint16_t s16 = PK ? (uint16_t)(sp >> (16 * gs)) : LS ? s_lds[s_row_lds + g] : ss[gs];
         const double sc = (double)(float)__builtin_bit_cast(_Float16, s16);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -294,9 +313,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 
     u32x4 ring[D][2];
     uint16_t sring[D][2];
+    uint32_t pring[D];
     if (full > 0) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u], sring[u], slot(u), false);
+        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u], sring[u], pring[u], slot(u), false);
     }
     if constexpr (LS) {
         if (full > 0)
@@ -322,11 +342,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 #pragma unroll
             for (int u = 0; u < D; ++u) {
                 wait_vm<kLoadsPerStage * (D - 1)>();
-                swap16(ring[u][0], ring[u][1]);
-                step(ring[u], sring[u], slot(u), 0, g);
-                step(ring[u], sring[u], slot(u), 1, g + 1);
+                if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
+                step(ring[u], sring[u], pring[u], slot(u), 0, g);
+                step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
                 __builtin_amdgcn_sched_barrier(0);
-                load_stage(g + 2 * D, ring[u], sring[u], slot(u), false);
+                load_stage(g + 2 * D, ring[u], sring[u], pring[u], slot(u), false);
                 __builtin_amdgcn_sched_barrier(0);
                 g += 2;
             }
@@ -337,9 +357,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
             constexpr int u = decltype(U)::value;
             if constexpr (u <= D - 2) {  // a tail has at most D - 1 stages
                 wait_vm<kLoadsPerStage * (D - 1 - u)>();
-                swap16(ring[u][0], ring[u][1]);
-                step(ring[u], sring[u], slot(u), 0, g);
-                step(ring[u], sring[u], slot(u), 1, g + 1);
+                if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
+                step(ring[u], sring[u], pring[u], slot(u), 0, g);
+                step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
                 g += 2;
             }
         };
@@ -356,12 +376,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     if (odd) {
         // the row's last group (slice 7 when K/32 is odd); the ring is drained
         // and slot 0's region of this wave is free
+        // (packed: the block of the last pair, whose second group is padding)
         u32x4 w1[2];
         uint16_t s1[2];
-        load_stage(g_end - 1, w1, s1, xr0, true);
+        uint32_t p1;
+        load_stage(g_end - 1, w1, s1, p1, xr0, true);
         wait_vm<0>();
-        swap16(w1[0], w1[1]);
-        step(w1, s1, xr0, 0, g_end - 1);
+        if constexpr (!PK) swap16(w1[0], w1[1]);
+        step(w1, s1, p1, xr0, 0, g_end - 1);
     }
 
     // Left fold of the 8 slice sums, ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7,
@@ -739,13 +761,13 @@ const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     static const char* const tiles[2][2] = {{"gemm_w8g32_tiles<1, false>", "gemm_w8g32_tiles<1, true>"},
                                             {"gemm_w8g32_tiles<2, false>", "gemm_w8g32_tiles<2, true>"}};
     static const char* const split_lds[4][3] = {
-        {"gemm_w8g32_split_lds<1, 2, true, 0>", "gemm_w8g32_split_lds<1, 3, true, 0>", ""},
-        {"gemm_w8g32_split_lds<2, 2, true, 0>", "gemm_w8g32_split_lds<2, 3, true, 0>", ""},
-        {"gemm_w8g32_split_lds<3, 2, true, 0>", "", ""},
-        {"gemm_w8g32_split_lds<4, 2, true, 0>", "", ""}};
+        {"gemm_w8g32_split_lds<1, 2, true, 0, false>", "gemm_w8g32_split_lds<1, 3, true, 0, false>", ""},
+        {"gemm_w8g32_split_lds<2, 2, true, 0, false>", "gemm_w8g32_split_lds<2, 3, true, 0, false>", ""},
+        {"gemm_w8g32_split_lds<3, 2, true, 0, false>", "", ""},
+        {"gemm_w8g32_split_lds<4, 2, true, 0, false>", "", ""}};
     static const char* const split_lds_gs[4] = {
-        "gemm_w8g32_split_lds<1, 3, false, 0>", "gemm_w8g32_split_lds<2, 3, false, 0>",
-        "gemm_w8g32_split_lds<3, 2, false, 0>", "gemm_w8g32_split_lds<4, 2, false, 0>"};
+        "gemm_w8g32_split_lds<1, 3, false, 0, false>", "gemm_w8g32_split_lds<2, 3, false, 0, false>",
+        "gemm_w8g32_split_lds<3, 2, false, 0, false>", "gemm_w8g32_split_lds<4, 2, false, 0, false>"};
     if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
     const LinearPlan p = plan_linear(N, K, T_pad, S);
     switch (p.kind) {
@@ -756,7 +778,7 @@ const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     }
 }
 
-template <int EPI>
+template <int EPI, bool PK = false>
 static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
                         uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                         hipStream_t stream) {
@@ -765,8 +787,9 @@ static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S,
     const dim3 block(kGemmThreads);
 #define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                     \
     case TP * 16 + D * 2 + LS:                                                                          \
-        hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D, LS, EPI>), grid, block, 0, stream, W, S, X, Y, N, K, t, \
-                           ldx, ldy, ep);                                                               \
+        if constexpr (!(PK && LS))                                                                      \
+            hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D, LS, EPI, PK>), grid, block, 0, stream, W, S, X, Y, N, \
+                               K, t, ldx, ldy, ep);                                                     \
         break;
     switch (p.tp16 * 16 + p.depth * 2 + (p.lds_scales ? 1 : 0)) {
         W8I_SPLIT_LAUNCH(1, 2, true)
@@ -797,6 +820,12 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
         default:
             return W8I_ESHAPE;
     }
+}
+
+int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X, int t, int T_pad, uint16_t* Y,
+                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+    const LinearPlan p = plan_split(T_pad / 16, 0);  // scales come with each stage
+    return launch_split<kEpiStore, true>(p, Wp, Sp, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
 }
 
 int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,

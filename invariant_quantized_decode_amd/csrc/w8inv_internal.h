@@ -32,6 +32,14 @@ struct LinearEpilogue {
 
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                   int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+// the projection over weights and scales in the packed layout (w8_pack)
+int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X, int t, int T_pad, uint16_t* Y,
+                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+// bytes of the packed layout of an [N, K] projection: 32-row strips x ceil(K/64) blocks
+inline int64_t packed_weight_bytes(int64_t N, int64_t K) { return (N + 31) / 32 * ((K / kGroup + 1) / 2) * 2048; }
+inline int64_t packed_scale_bytes(int64_t N, int64_t K) { return (N + 31) / 32 * ((K / kGroup + 1) / 2) * 128; }
+int launch_pack(const int8_t* W, const uint16_t* S, int64_t N, int64_t K, int8_t* Wp, uint16_t* Sp,
+                hipStream_t stream);
 // the projection with a fused epilogue (always the LDS-staged split kernel);
 // for kEpiSwiGLU, N is the projection's 2F rows and y has F columns
 int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,

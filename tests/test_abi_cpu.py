@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -30,13 +30,13 @@ def test_every_declared_symbol_is_exported():
 def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
     """The kernel-name query is host-only; it names one kernel per (N, K, T_pad, scales alignment)."""
     q = L.w8_linear_invariant_kernel
-    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true, 0>"
-    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false, 0>"  # scales not 16-byte aligned
+    assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true, 0, false>"
+    assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false, 0, false>"  # scales not 16-byte aligned
     assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2, true>"
     assert q(248320, 5120, 32, fake(4098)) == b"gemm_w8g32_tiles<2, false>"   # scales not 16-byte aligned
     assert q(248320, 5088, 16, fake(4096)) == b"gemm_w8g32_tiles<1, false>"   # K/32 = 159
-    assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true, 0>"
-    assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false, 0>"  # scales too large for LDS
+    assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true, 0, false>"
+    assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false, 0, false>"  # scales too large for LDS
     for bad in ((6144, 5100, 32), (0, 5120, 32), (6144, 5120, 24), (6144, 5120, 80)):
         assert q(*bad, fake(4096)) == b""
 
@@ -108,6 +108,29 @@ def linear_swiglu(W=A, S=A, X=A, t=4, T=32, Y=A, F=64, K=256, ldx=256, ldy=64):
 ])
 def test_linear_swiglu_rejects_invalid_arguments(kw, code):
     assert linear_swiglu(**kw) == code
+
+
+def test_pack_sizes_and_validation():
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.w8_pack_bytes(6144, 5120, ctypes.byref(wb), ctypes.byref(sb)) == 0
+    assert (wb.value, sb.value) == (192 * 80 * 2048, 192 * 80 * 128)     # whole strips x pairs of groups
+    assert L.w8_pack_bytes(33, 160, ctypes.byref(wb), ctypes.byref(sb)) == 0
+    assert (wb.value, sb.value) == (2 * 3 * 2048, 2 * 3 * 128)          # ragged rows, odd K/32 padded
+    assert L.w8_pack_bytes(33, 100, ctypes.byref(wb), ctypes.byref(sb)) == -2
+    assert L.w8_pack_bytes(1 << 20, 8192, ctypes.byref(wb), ctypes.byref(sb)) == -2   # 8 GiB of codes
+    assert L.w8_pack_bytes(64, 256, None, ctypes.byref(sb)) == -1
+    assert L.w8_pack(fake(A), fake(A), 64, 256, fake(A + 8), fake(A), None) == -3
+    assert L.w8_pack(fake(A), None, 64, 256, fake(A), fake(A), None) == -1
+    assert L.w8_pack(fake(A), fake(A), 64, 250, fake(A), fake(A), None) == -2
+
+
+def test_packed_linear_validation():
+    f = L.w8_linear_invariant_packed
+    assert f(fake(A), fake(A), fake(A), 0, 32, fake(A), 64, 256, 256, 64, None) == 0
+    assert f(fake(A), fake(A), fake(A), 4, 24, fake(A), 64, 256, 256, 64, None) == -4
+    assert f(fake(A), fake(A + 4), fake(A), 4, 32, fake(A), 64, 256, 256, 64, None) == -3
+    assert f(None, fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 64, None) == -1
+    assert f(fake(A), fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 32, None) == -2
 
 
 def logprob(Lg=A, T=A, block=4096, out=A, t=4, V=248320, ldl=248320, ws=A, wsb=1 << 20):

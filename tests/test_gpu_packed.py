@@ -1,0 +1,95 @@
+"""The packed weight layout on the GPU, through the C ABI.
+
+w8_pack is byte work: its output must equal the layout the header defines, element for element
+(checked against a numpy construction of that layout).  The projection over the packed layout
+runs the same K plan, so it must give the bits of w8_linear_invariant on the original layout
+for every argument; parity with the oracle (2 bf16 ulps) then carries over, and is checked
+directly on one shape as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import within_bf16_ulps
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import invariant_quantized_decode_amd as w8  # noqa: E402
+from tests.gpu_util import bf16, bits, f16, i8, say  # noqa: E402
+
+
+def layout(q, s):
+    """The packed layout, built from its definition with numpy indexing."""
+    N, K = q.shape
+    G = K // 32
+    P = (G + 1) // 2
+    strips = (N + 31) // 32
+    qp = np.zeros((strips * 32, P * 64), dtype=np.int8)
+    qp[:N, :K] = q
+    sp = np.zeros((strips * 32, P * 2), dtype=np.uint16)
+    sp[:N, :G] = s
+    # [s, r, p, gs, c, b] -> [s, p, gs, c, r, b]
+    codes = qp.reshape(strips, 32, P, 2, 2, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
+    # [s, r, p, gs] -> [s, p, r, gs]
+    scales = sp.reshape(strips, 32, P, 2).transpose(0, 2, 1, 3).reshape(-1)
+    return codes, scales
+
+
+@pytest.mark.parametrize("N,K", [(64, 256), (33, 160), (100, 1056), (1, 32), (6144, 5120)])
+def test_pack_matches_the_defined_layout(N, K):
+    say(f"case pack N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    Wp, Sp = w8.w8_pack(i8(q), f16(s))
+    codes, scales = layout(q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(Wp.cpu().numpy(), codes)
+    assert np.array_equal(Sp.cpu().numpy().view(np.uint16), scales)
+
+
+CASES = [  # N, K, T_pad: headline shape, ragged rows, odd K/32, empty slices, every T_pad, long K
+    (6144, 5120, 32),
+    (257, 1056, 48),
+    (33, 160, 16),
+    (64, 32, 16),
+    (1000, 4096, 64),
+    (40, 17408, 64),
+    (24, 36896, 16),
+    (5120, 6144, 32),
+]
+
+
+@pytest.mark.parametrize("N,K,T_pad", CASES)
+def test_packed_projection_gives_the_plain_bits(N, K, T_pad):
+    say(f"case packed N={N} K={K} T_pad={T_pad}")
+    rng = np.random.default_rng(3 * N + K)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    x = synth.draw_acts(rng, T_pad, K)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    full = bits(w8.w8_linear_invariant(Wd, Sd, Xd, T_pad, T_pad))
+    assert np.array_equal(bits(w8.w8_linear_invariant_packed(Wp, Sp, Xd, T_pad, T_pad, N)), full)
+    for t in (1, T_pad // 2 + 1):
+        perm = rng.permutation(T_pad)[:t]
+        got = bits(w8.w8_linear_invariant_packed(Wp, Sp, bf16(x[perm]), t, T_pad, N))
+        assert np.array_equal(got, full[perm])
+
+
+def test_packed_projection_matches_oracle():
+    N, K, t, T_pad = 300, 2080, 20, 32
+    rng = np.random.default_rng(77)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    x = synth.draw_acts(rng, t, K)
+    Wp, Sp = w8.w8_pack(i8(q), f16(s))
+    y = bits(w8.w8_linear_invariant_packed(Wp, Sp, bf16(x), t, T_pad, N))
+    ok, err = within_bf16_ulps(y, oracle.w8_linear(q, s, x), 2.0)
+    say(f"packed vs oracle: max err {float(err.max()):.3f} ulp")
+    assert ok.all()
