@@ -128,8 +128,9 @@ const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, cons
  *   overlap between the inputs and the outputs.
  * w8_linear_invariant_packed: as w8_linear_invariant (x, y, t, T_pad, N, K,
  *   ldx, ldy and their rules), with Wp / Sp from w8_pack(N, K) (16-byte
- *   aligned).  No workspace.  Any N (one kernel family: the LDS-staged split
- *   kernel with per-stage scale loads).
+ *   aligned).  No workspace.  Any N: the persistent kernel where the plain
+ *   layout runs it (T_pad <= 32, N >= 131072), else the LDS-staged split
+ *   kernel, both with per-stage scale loads.
  * ------------------------------------------------------------------------- */
 int w8_pack_bytes(int64_t N, int64_t K, size_t *wp_bytes, size_t *sp_bytes);
 
@@ -139,6 +140,11 @@ int w8_pack(const int8_t *W_q, const uint16_t *scales, int64_t N, int64_t K, int
 int w8_linear_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint16_t *x, int32_t t,
                                int32_t T_pad, uint16_t *y, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
                                void *stream);
+
+/* Name of the kernel w8_linear_invariant_packed runs (static storage; "" for
+ * arguments it would reject): a function of N and T_pad, never of t.  Pure host
+ * function. */
+const char *w8_linear_invariant_packed_kernel(int64_t N, int64_t K, int32_t T_pad);
 
 /* ---------------------------------------------------------------------------
  * Fused W8 projection epilogues.

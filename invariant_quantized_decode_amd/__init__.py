@@ -26,7 +26,7 @@ STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: 
 
 EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
            "w8_linear_invariant_kernel", "w8_linear_add_invariant", "w8_linear_swiglu_invariant",
-           "w8_pack_bytes", "w8_pack", "w8_linear_invariant_packed",
+           "w8_pack_bytes", "w8_pack", "w8_linear_invariant_packed", "w8_linear_invariant_packed_kernel",
            "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32")
 
@@ -54,6 +54,8 @@ def _load():
     L.w8_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
     L.w8_pack.argtypes = [P, P, I64, I64, P, P, P]
     L.w8_linear_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
+    L.w8_linear_invariant_packed_kernel.argtypes = [I64, I64, I32]
+    L.w8_linear_invariant_packed_kernel.restype = ctypes.c_char_p
     L.vocab_block_logprob_workspace_bytes.argtypes = [I32, I64, I32]
     L.vocab_block_logprob_workspace_bytes.restype = SZ
     L.vocab_block_logprob.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
@@ -223,6 +225,11 @@ def w8_linear_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tens
                                          ctypes.c_void_p(_stream(Wp.device)))
     _check("w8_linear_invariant_packed", st)
     return y
+
+
+def w8_linear_invariant_packed_kernel(N: int, K: int, T_pad: int) -> str:
+    """Name of the kernel w8_linear_invariant_packed runs for this shape.  Host-side only."""
+    return _lib.w8_linear_invariant_packed_kernel(int(N), int(K), int(T_pad)).decode()
 
 
 def w8_linear_invariant_kernel(N: int, K: int, T_pad: int, scales: torch.Tensor | None = None) -> str:

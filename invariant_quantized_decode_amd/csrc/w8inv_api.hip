@@ -102,6 +102,11 @@ int w8_linear_invariant_packed(const int8_t* Wp, const uint16_t* Sp, const uint1
     return launch_linear_packed(Wp, Sp, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
 }
 
+const char* w8_linear_invariant_packed_kernel(int64_t N, int64_t K, int32_t T_pad) {
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return "";
+    return linear_packed_kernel_name(N, K, T_pad);
+}
+
 int w8_linear_add_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const uint16_t* residual,
                             int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldr,
                             int64_t ldy, void* stream) {

@@ -454,7 +454,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
 constexpr int kBlockStages = 4;        // stages per block
 
-template <int TP16, bool SC>
+// PK: packed layout (w8_pack): each stage's weights are the strip's 2 KB block
+// and its scales one 128-byte line, loaded with the stage.
+template <int TP16, bool SC, bool PK>
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, int ntiles) {
@@ -463,7 +465,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     constexpr int kStageBytes = NT * kXTileBytes;                 // one stage's activations
     constexpr int kBlockBytes = kBlockStages * kStageBytes;       // one block's
     constexpr int kXLoads = kBlockBytes / kLdsDmaBytes / kTileStrips;  // direct loads per wave per block
-    constexpr int LW = SC ? 2 : 4;                                // loads per stage (weights [+ scales])
+    static_assert(!(SC && PK), "packed scales come with each stage");
+    constexpr int LW = SC ? 2 : PK ? 3 : 4;                       // loads per stage (weights [+ scales])
     constexpr int LX = kXLoads;                                   // activation loads per block
     constexpr int LS = SC ? 1 : 0;                                // scale-chunk loads per block
     // one array per buffer, so each buffer's direct loads are told apart
@@ -479,10 +482,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     const int nb = my_tiles * nbt;                                // blocks of this workgroup
     const int r = lane & 31, c = lane >> 5;
 
-    const __amdgpu_buffer_rsrc_t w_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(N * K), 0x00020000);
+    // packed layout: whole strips of P = ceil(G/2) stage blocks (2 KB of codes, 128 bytes of scales)
+    const int64_t P = (G + 1) / 2;
+    const int64_t strips = (N + kRows - 1) / kRows;
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(PK ? strips * P * 2048 : N * K), 0x00020000);
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(N * G * 2), 0x00020000);
+        const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(PK ? strips * P * 128 : N * G * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, 0x00020000);
@@ -512,6 +518,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     struct WStage {
         u32x4 w[2];
         uint16_t s[2];
+        uint32_t sp;  // packed: the row's two scales
     };
     // weights (and per-stage scales) of stage u of block b
     auto load_stage = [&](int b, int u, WStage& st) {
@@ -520,6 +527,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
         const int g1 = g + 1 < G ? g + 1 : g;  // odd G: the last stage repeats its group
         const int64_t row0 = strip_row(b < nb ? b : nb - 1);
+        if constexpr (PK) {
+            // the strip's block of pair g / 2 (strips past the last read the
+            // last one: valid memory, never stored); lane l takes bytes
+            // 16 l .. 16 l + 15 of each 1 KB half and its row's scale pair
+            const int64_t strip = row0 / kRows < strips ? row0 / kRows : strips - 1;
+            const uint32_t blk = (uint32_t)(strip * P + g / 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                st.w[i] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, blk * 2048u + 1024u * i + 16u * lane, 0, 0));
+            st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, blk * 128u + 4u * r, 0, 0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int64_t row = row0 + 16 * i + (lane & 15);
@@ -616,7 +636,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             WStage& cur = ring[u];
             const int g = g0 + 2 * u;
             if (live && g < G) {
-                swap16(cur.w[0], cur.w[1]);
+                if constexpr (!PK) swap16(cur.w[0], cur.w[1]);
                 while (kslice_begin(G, slice + 1) <= g) fold_slice();
                 const int ng = (g + 1 < G) ? 2 : 1;
 #pragma unroll
@@ -627,6 +647,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                     uint16_t s16;
                     if constexpr (SC)
                         s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
+                    else if constexpr (PK)
+                        s16 = (uint16_t)(cur.sp >> (16 * gs));
                     else
                         s16 = cur.s[gs];
                     const double scale = (double)(float)__builtin_bit_cast(_Float16, s16);
@@ -677,34 +699,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
 // to keep every CU busy for several tiles.
 static int tile_count(int64_t N) { return (int)((N + kTileStrips * kRows - 1) / (kTileStrips * kRows)); }
 
+// scales: 0 per-stage 2-byte loads, 1 eight scales per 16-byte load (SC), 2 packed layout (PK)
 static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
-                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, bool sc, hipStream_t stream) {
+                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, int scales, hipStream_t stream) {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return W8I_EHIP;
     const int ntiles = tile_count(N);
     const dim3 grid((unsigned)(ntiles < ncu ? ntiles : ncu)), block(kGemmThreads);
-    switch (T_pad / 16) {
-        case 1:
-            if (sc)
-                hipLaunchKernelGGL((gemm_w8g32_tiles<1, true>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
-                                   ntiles);
-            else
-                hipLaunchKernelGGL((gemm_w8g32_tiles<1, false>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
-                                   ntiles);
-            break;
-        case 2:
-            if (sc)
-                hipLaunchKernelGGL((gemm_w8g32_tiles<2, true>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
-                                   ntiles);
-            else
-                hipLaunchKernelGGL((gemm_w8g32_tiles<2, false>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy,
-                                   ntiles);
-            break;
-        default:
-            return W8I_ET;
+#define W8I_TILES_LAUNCH(TP, SCV, PKV)                                                                    \
+    hipLaunchKernelGGL((gemm_w8g32_tiles<TP, SCV, PKV>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, \
+                       ntiles)
+    switch (T_pad / 16 * 4 + scales) {
+        case 4: W8I_TILES_LAUNCH(1, false, false); break;
+        case 5: W8I_TILES_LAUNCH(1, true, false); break;
+        case 6: W8I_TILES_LAUNCH(1, false, true); break;
+        case 8: W8I_TILES_LAUNCH(2, false, false); break;
+        case 9: W8I_TILES_LAUNCH(2, true, false); break;
+        case 10: W8I_TILES_LAUNCH(2, false, true); break;
+        default: return W8I_ET;
     }
+#undef W8I_TILES_LAUNCH
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 
@@ -758,8 +774,9 @@ static LinearPlan plan_epilogue(int epi, int64_t N, int64_t K, int T_pad, const 
 }
 
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
-    static const char* const tiles[2][2] = {{"gemm_w8g32_tiles<1, false>", "gemm_w8g32_tiles<1, true>"},
-                                            {"gemm_w8g32_tiles<2, false>", "gemm_w8g32_tiles<2, true>"}};
+    static const char* const tiles[2][2] = {
+        {"gemm_w8g32_tiles<1, false, false>", "gemm_w8g32_tiles<1, true, false>"},
+        {"gemm_w8g32_tiles<2, false, false>", "gemm_w8g32_tiles<2, true, false>"}};
     static const char* const split_lds[4][3] = {
         {"gemm_w8g32_split_lds<1, 2, true, 0, false>", "gemm_w8g32_split_lds<1, 3, true, 0, false>", ""},
         {"gemm_w8g32_split_lds<2, 2, true, 0, false>", "gemm_w8g32_split_lds<2, 3, true, 0, false>", ""},
@@ -776,6 +793,18 @@ const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
             return p.lds_scales ? split_lds[p.tp16 - 1][p.depth - 2] : split_lds_gs[p.tp16 - 1];
         default: return "";
     }
+}
+
+const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad) {
+    static const char* const tiles[2] = {"gemm_w8g32_tiles<1, false, true>", "gemm_w8g32_tiles<2, false, true>"};
+    static const char* const split[4] = {
+        "gemm_w8g32_split_lds<1, 3, false, 0, true>", "gemm_w8g32_split_lds<2, 3, false, 0, true>",
+        "gemm_w8g32_split_lds<3, 2, false, 0, true>", "gemm_w8g32_split_lds<4, 2, false, 0, true>"};
+    (void)K;
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return tiles[T_pad / 16 - 1];
+    const LinearPlan p = plan_split(T_pad / 16, 0);
+    return p.depth == (T_pad <= 32 ? 3 : 2) ? split[T_pad / 16 - 1] : "";
 }
 
 template <int EPI, bool PK = false>
@@ -814,7 +843,7 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
     const LinearPlan p = plan_linear(N, K, T_pad, S);
     switch (p.kind) {
         case LinearKernel::kTiles:
-            return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, p.lds_scales, stream);
+            return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, p.lds_scales ? 1 : 0, stream);
         case LinearKernel::kSplitLds:
             return launch_split<kEpiStore>(p, W, S, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
         default:
@@ -824,6 +853,9 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
 
 int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+    // the persistent kernel where it runs the plain layout, else the split kernel
+    if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256)
+        return launch_tiles(Wp, Sp, X, t, T_pad, Y, N, K, ldx, ldy, 2, stream);
     const LinearPlan p = plan_split(T_pad / 16, 0);  // scales come with each stage
     return launch_split<kEpiStore, true>(p, Wp, Sp, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
 }

@@ -46,6 +46,7 @@ int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const ui
                            uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                            hipStream_t stream);
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S);
+const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad);
 
 size_t logprob_workspace_bytes(int t, int64_t V, int block);
 int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -32,9 +32,9 @@ def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
     q = L.w8_linear_invariant_kernel
     assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true, 0, false>"
     assert q(6144, 5120, 32, fake(4098)) == b"gemm_w8g32_split_lds<2, 3, false, 0, false>"  # scales not 16-byte aligned
-    assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2, true>"
-    assert q(248320, 5120, 32, fake(4098)) == b"gemm_w8g32_tiles<2, false>"   # scales not 16-byte aligned
-    assert q(248320, 5088, 16, fake(4096)) == b"gemm_w8g32_tiles<1, false>"   # K/32 = 159
+    assert q(248320, 5120, 32, fake(4096)) == b"gemm_w8g32_tiles<2, true, false>"
+    assert q(248320, 5120, 32, fake(4098)) == b"gemm_w8g32_tiles<2, false, false>"   # scales not 16-byte aligned
+    assert q(248320, 5088, 16, fake(4096)) == b"gemm_w8g32_tiles<1, false, false>"   # K/32 = 159
     assert q(34816, 5120, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, true, 0, false>"
     assert q(5120, 17408, 64, fake(4096)) == b"gemm_w8g32_split_lds<4, 2, false, 0, false>"  # scales too large for LDS
     for bad in ((6144, 5100, 32), (0, 5120, 32), (6144, 5120, 24), (6144, 5120, 80)):
@@ -122,6 +122,15 @@ def test_pack_sizes_and_validation():
     assert L.w8_pack(fake(A), fake(A), 64, 256, fake(A + 8), fake(A), None) == -3
     assert L.w8_pack(fake(A), None, 64, 256, fake(A), fake(A), None) == -1
     assert L.w8_pack(fake(A), fake(A), 64, 250, fake(A), fake(A), None) == -2
+
+
+def test_packed_kernel_query():
+    q = L.w8_linear_invariant_packed_kernel
+    assert q(6144, 5120, 32) == b"gemm_w8g32_split_lds<2, 3, false, 0, true>"
+    assert q(34816, 5120, 64) == b"gemm_w8g32_split_lds<4, 2, false, 0, true>"
+    assert q(248320, 5120, 32) == b"gemm_w8g32_tiles<2, false, true>"
+    assert q(248320, 5120, 64) == b"gemm_w8g32_split_lds<4, 2, false, 0, true>"
+    assert q(6144, 5100, 32) == b"" and q(6144, 5120, 24) == b""
 
 
 def test_packed_linear_validation():

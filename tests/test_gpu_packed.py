@@ -82,6 +82,22 @@ def test_packed_projection_gives_the_plain_bits(N, K, T_pad):
         assert np.array_equal(got, full[perm])
 
 
+@pytest.mark.parametrize("N,K,T_pad", [(131172, 1024, 32), (131149, 5088, 32), (131105, 96, 16)])
+def test_packed_persistent_kernel_gives_the_plain_bits(N, K, T_pad):
+    """N >= 131072 at T_pad <= 32 runs the persistent kernel on both layouts (ragged tiles, odd K/32)."""
+    say(f"case packed persistent N={N} K={K} T_pad={T_pad}")
+    assert w8.w8_linear_invariant_packed_kernel(N, K, T_pad).startswith("gemm_w8g32_tiles")
+    rng = np.random.default_rng(N + K)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    x = synth.draw_acts(rng, T_pad, K)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    for t in (1, T_pad):
+        plain = bits(w8.w8_linear_invariant(Wd, Sd, Xd, t, T_pad))
+        assert np.array_equal(bits(w8.w8_linear_invariant_packed(Wp, Sp, Xd, t, T_pad, N)), plain)
+
+
 def test_packed_projection_matches_oracle():
     N, K, t, T_pad = 300, 2080, 20, 32
     rng = np.random.default_rng(77)
