@@ -1,14 +1,18 @@
 """Throughput of the batch-invariant W8A16 decode projection on one MI355X.
 
-One step = one call of w8_linear_invariant on the 6144x5120 projection
-(int8 G32 weights, fp16 scales, bf16 activations) at the fixed width
-T_pad = 32 with t = 32 real columns -- the whole hot path for this workload.
-The weights rotate over enough device copies (>= 1 GiB) that the 256 MB
-Infinity Cache cannot serve them, steps are replayed from HIP graphs, and the
-time of the timed steps is taken with HIP events on the stream they run on.
-The same is measured at t = 1.  Prints one JSON line.
+One step = one call of the projection on the 6144x5120 workload (int8 G32
+weights, fp16 scales, bf16 activations) at the fixed width T_pad = 32 with
+t = 32 real columns -- the whole hot path for this workload.  The weights are
+held in the packed layout (w8_pack, prepared once when the weights are loaded,
+outside the timed region) and the step is w8_linear_invariant_packed; the same
+is measured on the plain row-major layout (w8_linear_invariant) and reported
+beside it.  Both give the same bits.  The weights rotate over enough device
+copies (>= 1 GiB) that the 256 MB Infinity Cache cannot serve them, steps are
+replayed from HIP graphs, and the time of the timed steps is taken with HIP
+events on the stream they run on.  The same is measured at t = 1.  Prints one
+JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1] [--pmc-pass] [--all]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1] [--layout packed|plain] [--pmc-pass] [--all]
 """
 from __future__ import annotations
 
@@ -39,6 +43,8 @@ def parse():
     p.add_argument("--all", action="store_true",
                    help="instead of the bench line: one JSON line per workload (every configured projection and "
                         "the chain's, at t=1 and t=T_pad, and the head's logprob), with the CPU oracle on a row sample")
+    p.add_argument("--layout", choices=("packed", "plain"), default="packed",
+                   help="weight layout of the headline step (the other one is reported beside it)")
     p.add_argument("--pmc-pass", action="store_true",
                    help="for rocprofv3 --pmc: a few plain launches at t=T_pad and t=1, then a plain 512 MiB "
                         "device copy (the calibration for the HBM byte counters); prints one short JSON line")
@@ -73,52 +79,66 @@ def main():
     copies = max(1, math.ceil((1 << 30) / wbytes))
     Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
     Ss = [S0] + [S0.clone() for _ in range(copies - 1)]
+    Ps = [w8.w8_pack(Ws[i], Ss[i]) for i in range(copies)]  # the packed layout, once per copy
     X = torch.from_numpy(pool.view(np.int16)).to(dev).view(torch.bfloat16)
     Y = torch.empty((T_pad, N), dtype=torch.bfloat16, device=dev)
 
-    kernel = w8.w8_linear_invariant_kernel(N, K, T_pad, S0)
+    def step(layout: str, c: int, Xt, t: int, y):
+        if layout == "packed":
+            return w8.w8_linear_invariant_packed(Ps[c][0], Ps[c][1], Xt, t, T_pad, N, y=y)
+        return w8.w8_linear_invariant(Ws[c], Ss[c], Xt, t, T_pad, y=y)
+
+    def kernel_of(layout: str) -> str:
+        if layout == "packed":
+            return w8.w8_linear_invariant_packed_kernel(N, K, T_pad)
+        return w8.w8_linear_invariant_kernel(N, K, T_pad, S0)
+
+    layout, other = args.layout, ("plain" if args.layout == "packed" else "packed")
+    kernel = kernel_of(layout)
     if args.pmc_pass:
         for t in (T_pad, 1):
             for i in range(3):
-                w8.w8_linear_invariant(Ws[i % copies], Ss[i % copies], X[:t], t, T_pad, y=Y)
+                step(layout, i % copies, X[:t], t, Y)
         torch.cuda.synchronize()
         a = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_pass": case.name, "kernel": kernel, "launches_per_t": 3, "t": [T_pad, 1],
-                          "copy_bytes": a.numel(), "alg_bytes_t_pad": wbytes + 2 * T_pad * (K + N)}), flush=True)
+        print(json.dumps({"pmc_pass": case.name, "layout": layout, "kernel": kernel, "launches_per_t": 3,
+                          "t": [T_pad, 1], "copy_bytes": a.numel(),
+                          "alg_bytes_t_pad": wbytes + 2 * T_pad * (K + N)}), flush=True)
         return
 
-    # ---- t-invariance on this workload: every pool column keeps its bits for t = 1..32
-    base = w8.w8_linear_invariant(W0, S0, X, T_pad, T_pad).clone()
+    # ---- t-invariance on this workload: every pool column keeps its bits for t = 1..32, on both
+    # layouts, and the two layouts agree bit for bit
+    base = step("plain", 0, X, T_pad, None).clone()
     inv_ok = True
     for t in range(1, T_pad + 1):
         cols = torch.from_numpy(d["perms"][t]).to(dev)
-        y = w8.w8_linear_invariant(W0, S0, X[cols].contiguous(), t, T_pad)
-        inv_ok &= bool(torch.equal(y.view(torch.int16), base[cols].view(torch.int16)))
+        for lay in ("plain", "packed"):
+            y = step(lay, 0, X[cols].contiguous(), t, None)
+            inv_ok &= bool(torch.equal(y.view(torch.int16), base[cols].view(torch.int16)))
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream(device=dev)
 
-    def capture(t: int, count: int, start: int):
+    def capture(lay: str, t: int, count: int, start: int):
         g = torch.cuda.CUDAGraph()
         Xt = X[:t]
         with torch.cuda.stream(stream):
-            w8.w8_linear_invariant(Ws[0], Ss[0], Xt, t, T_pad, y=Y)  # warm the launch path
+            step(lay, 0, Xt, t, Y)  # warm the launch path
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=stream):
                 for i in range(count):
-                    c = (start + i) % copies
-                    w8.w8_linear_invariant(Ws[c], Ss[c], Xt, t, T_pad, y=Y)
+                    step(lay, (start + i) % copies, Xt, t, Y)
         return g
 
-    def measure(t: int, steps: int, warmup: int):
+    def measure(lay: str, t: int, steps: int, warmup: int):
         R = copies
-        g_full = capture(t, R, 0)
+        g_full = capture(lay, t, R, 0)
         rem = steps % R
-        g_rem = capture(t, rem, 0) if rem else None
+        g_rem = capture(lay, t, rem, 0) if rem else None
         with torch.cuda.stream(stream):
             for _ in range(max(1, math.ceil(warmup / R))):
                 g_full.replay()
@@ -148,8 +168,11 @@ def main():
             alg_bytes=alg_bytes,
         )
 
-    full = measure(T_pad, args.steps, args.warmup)
-    one = measure(1, args.steps, args.warmup)
+    full = measure(layout, T_pad, args.steps, args.warmup)
+    one = measure(layout, 1, args.steps, args.warmup)
+    alt_steps = max(copies, args.steps // 3)
+    alt_full = measure(other, T_pad, alt_steps, args.warmup // 3)
+    alt_one = measure(other, 1, alt_steps, args.warmup // 3)
 
     # context: a plain device-to-device copy of 1 GiB (read + write bytes / time)
     a = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
@@ -170,7 +193,8 @@ def main():
     if os.path.exists(tpath):
         from invariant_quantized_decode_amd import kernel_source_digest
         rec = json.load(open(tpath))
-        if rec.get("kernel_digest") == kernel_source_digest() and rec.get("workload") == case.name:
+        if rec.get("kernel_digest") == kernel_source_digest() and rec.get("workload") == case.name \
+                and rec.get("kernel") == kernel:
             traffic = rec.get("bytes_per_launch")
 
     roof = dict(bound="hbm", achieved=round(full["alg_gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -210,13 +234,20 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": case.name, "N": N, "K": K, "T_pad": T_pad, "t": T_pad,
-                   "weight_bytes": wbytes, "rotating_weight_copies": copies, "launch": "hipGraph replay"},
+                   "weight_bytes": wbytes, "rotating_weight_copies": copies, "launch": "hipGraph replay",
+                   "layout": layout + (" (w8_pack, prepared once outside the timed region)" if layout == "packed"
+                                       else " (row-major codes and scales as given)")},
         "hbm_frac_t_pad": r(full["weight_gbs"] / HBM_PEAK_GBS, 4),
         "tflops_t_pad": {"useful": r(full["tflops_useful"]), "executed": r(full["tflops_executed"]),
                          "mfma_frac_executed": r(full["tflops_executed"] / BF16_PEAK_TFLOPS, 4)},
         "t1": {"value": r(one["weight_gbs"], 1), "unit": "GB/s", "ms_per_step": r(one["ms_per_step"], 5),
                "hbm_frac": r(one["weight_gbs"] / HBM_PEAK_GBS, 4), "tflops_useful": r(one["tflops_useful"]),
                "tflops_executed": r(one["tflops_executed"])},
+        other + "_layout": {"kernel": kernel_of(other), "t_pad": {"value": r(alt_full["weight_gbs"], 1),
+                                                                 "ms_per_step": r(alt_full["ms_per_step"], 5),
+                                                                 "hbm_frac": r(alt_full["weight_gbs"] / HBM_PEAK_GBS, 4)},
+                            "t1": {"value": r(alt_one["weight_gbs"], 1), "ms_per_step": r(alt_one["ms_per_step"], 5),
+                                   "hbm_frac": r(alt_one["weight_gbs"] / HBM_PEAK_GBS, 4)}},
         "t_invariance": inv_ok,
         "device_copy_gbs": r(copy_gbs, 1),
         "roofline": roof,
@@ -236,6 +267,8 @@ def run_all(torch, w8, synth, dev, args):
     work = [(c.name, c.N, c.K, c.T_pad, c.scale_eps, "linear") for c in
             (synth.LINEAR_1024, synth.LINEAR_6144, synth.MLP_GATE_UP, synth.MLP_DOWN, synth.HEAD)]
     work += [(n, N, K, synth.CHAIN_T_PAD, 0.0, "linear") for n, N, K in chain]
+    # the same projections over the packed layout (w8_pack, prepared once per weight copy)
+    work += [(n, N, K, T, e, "packed") for n, N, K, T, e, _ in list(work)]
     # the chain's projections with their glue fused into the epilogue
     work += [("chain o + residual (fused) 5120x6144", 5120, 6144, synth.CHAIN_T_PAD, 0.0, "add"),
              ("chain gate+up + SwiGLU (fused) 34816x5120", 34816, 5120, synth.CHAIN_T_PAD, 0.0, "swiglu"),
@@ -254,6 +287,10 @@ def run_all(torch, w8, synth, dev, args):
         if op == "linear":
             kernel = w8.w8_linear_invariant_kernel(N, K, T_pad, Ss[0])
             call = lambda i, t: w8.w8_linear_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)  # noqa: E731
+        elif op == "packed":
+            Ps = [w8.w8_pack(Ws[i], Ss[i]) for i in range(copies)]
+            kernel = w8.w8_linear_invariant_packed_kernel(N, K, T_pad)
+            call = lambda i, t: w8.w8_linear_invariant_packed(Ps[i][0], Ps[i][1], X[:t], t, T_pad, N, y=Y)  # noqa
         elif op == "add":
             kernel = "gemm_w8g32_split_lds, residual-add epilogue"
             call = lambda i, t: w8.w8_linear_add_invariant(Ws[i], Ss[i], X[:t], R[:t], t, T_pad, y=Y)  # noqa: E731
@@ -289,13 +326,14 @@ def run_all(torch, w8, synth, dev, args):
             c0 = time.perf_counter()
             oracle.w8_linear(qh, sh, xh)
             csec = time.perf_counter() - c0
-            print(json.dumps({"workload": name, "kernel": kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
+            print(json.dumps({"workload": name + (" [packed]" if op == "packed" else ""), "kernel": kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
                               "weight_gbs": round(wbytes / sec / 1e9, 1),
                               "roofline_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
                               "tflops_useful": round(2.0 * N * K * t / sec / 1e12, 3),
                               "cpu_oracle_gbs": round(len(rows) * K * 1.0625 / csec / 1e9, 4),
                               "cpu_sample": f"{len(rows)} rows, {oracle.max_threads()} threads"}), flush=True)
         del Ws, Ss
+        Ps = None
         torch.cuda.empty_cache()
     # the chain's column-local glue at T_pad columns (graph-replayed; bytes = reads + writes)
     H, F, tg = synth.CHAIN_HIDDEN, synth.CHAIN_FFN, synth.CHAIN_T_PAD
