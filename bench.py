@@ -273,6 +273,7 @@ def run_all(torch, w8, synth, dev, args):
     work += [("chain o + residual (fused) 5120x6144", 5120, 6144, synth.CHAIN_T_PAD, 0.0, "add"),
              ("chain gate+up + SwiGLU (fused) 34816x5120", 34816, 5120, synth.CHAIN_T_PAD, 0.0, "swiglu"),
              ("chain down + residual (fused) 5120x17408", 5120, 17408, synth.CHAIN_T_PAD, 0.0, "add")]
+    work += [(n, N, K, T, e, op + "_packed") for n, N, K, T, e, op in list(work) if op in ("add", "swiglu")]
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     stream = torch.cuda.Stream(device=dev)
@@ -283,20 +284,29 @@ def run_all(torch, w8, synth, dev, args):
         Ss = [(torch.randn(N, K // 32, generator=g, device=dev).abs_() * 0.02 + eps).half() for _ in range(copies)]
         X = torch.randn(T_pad, K, generator=g, device=dev).to(torch.bfloat16)
         R = torch.randn(T_pad, N, generator=g, device=dev).to(torch.bfloat16)
-        Y = torch.empty((T_pad, N // 2 if op == "swiglu" else N), dtype=torch.bfloat16, device=dev)
+        Y = torch.empty((T_pad, N // 2 if op.startswith("swiglu") else N), dtype=torch.bfloat16, device=dev)
+        if op.endswith("packed"):
+            Ps = [w8.w8_pack(Ws[i], Ss[i]) for i in range(copies)]
         if op == "linear":
             kernel = w8.w8_linear_invariant_kernel(N, K, T_pad, Ss[0])
             call = lambda i, t: w8.w8_linear_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)  # noqa: E731
         elif op == "packed":
-            Ps = [w8.w8_pack(Ws[i], Ss[i]) for i in range(copies)]
             kernel = w8.w8_linear_invariant_packed_kernel(N, K, T_pad)
             call = lambda i, t: w8.w8_linear_invariant_packed(Ps[i][0], Ps[i][1], X[:t], t, T_pad, N, y=Y)  # noqa
         elif op == "add":
             kernel = "gemm_w8g32_split_lds, residual-add epilogue"
             call = lambda i, t: w8.w8_linear_add_invariant(Ws[i], Ss[i], X[:t], R[:t], t, T_pad, y=Y)  # noqa: E731
-        else:
+        elif op == "swiglu":
             kernel = "gemm_w8g32_split_lds, SwiGLU epilogue"
             call = lambda i, t: w8.w8_linear_swiglu_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y)  # noqa: E731
+        elif op == "add_packed":
+            kernel = "gemm_w8g32_split_lds, residual-add epilogue, packed layout"
+            call = lambda i, t: w8.w8_linear_add_invariant_packed(  # noqa: E731
+                Ps[i][0], Ps[i][1], X[:t], R[:t], t, T_pad, N, y=Y)
+        else:
+            kernel = "gemm_w8g32_split_lds, SwiGLU epilogue, packed layout"
+            call = lambda i, t: w8.w8_linear_swiglu_invariant_packed(  # noqa: E731
+                Ps[i][0], Ps[i][1], X[:t], t, T_pad, N // 2, y=Y)
         for t in (1, T_pad):
             reps = max(2, math.ceil(20000 / copies))  # about 20000 launches, fewer for the largest
             reps = min(reps, max(2, int(2e10 // (wbytes * copies))))
@@ -317,7 +327,7 @@ def run_all(torch, w8, synth, dev, args):
                 torch.cuda.synchronize()
             sec = e0.elapsed_time(e1) / 1e3 / (reps * copies)
             # algorithmic bytes: weights and scales, x, y (and the residual read)
-            alg = wbytes + 2 * t * K + 2 * t * Y.shape[1] + (2 * t * N if op == "add" else 0)
+            alg = wbytes + 2 * t * K + 2 * t * Y.shape[1] + (2 * t * N if op.startswith("add") else 0)
             # CPU oracle on a 64-row sample of the same projection
             rows = np.arange(0, N, max(1, N // 64))[:64]
             qh = Ws[0][rows].cpu().numpy()
@@ -326,7 +336,7 @@ def run_all(torch, w8, synth, dev, args):
             c0 = time.perf_counter()
             oracle.w8_linear(qh, sh, xh)
             csec = time.perf_counter() - c0
-            print(json.dumps({"workload": name + (" [packed]" if op == "packed" else ""), "kernel": kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
+            print(json.dumps({"workload": name + (" [packed]" if op.endswith("packed") else ""), "kernel": kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
                               "weight_gbs": round(wbytes / sec / 1e9, 1),
                               "roofline_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
                               "tflops_useful": round(2.0 * N * K * t / sec / 1e12, 3),

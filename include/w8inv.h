@@ -181,6 +181,19 @@ int w8_linear_swiglu_invariant(const int8_t *W_q, const uint16_t *scales, const 
                                int32_t t, int32_t T_pad, uint16_t *y, int64_t F, int64_t K,
                                int64_t ldx, int64_t ldy, void *stream);
 
+/* The same two over weights in the packed layout (w8_pack of the [N, K], resp.
+ * [2F, K], projection; Wp and Sp 16-byte aligned): the bits of the plain-layout
+ * call, as for w8_linear_invariant_packed.  Declared with the packed layout
+ * below. */
+int w8_linear_add_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint16_t *x,
+                                   const uint16_t *residual, int32_t t, int32_t T_pad, uint16_t *y,
+                                   int64_t N, int64_t K, int64_t ldx, int64_t ldr, int64_t ldy,
+                                   void *stream);
+
+int w8_linear_swiglu_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint16_t *x,
+                                      int32_t t, int32_t T_pad, uint16_t *y, int64_t F, int64_t K,
+                                      int64_t ldx, int64_t ldy, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Target-token logprob by fixed-width vocabulary blocks (LM-head epilogue).
  *

@@ -27,6 +27,7 @@ STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: 
 EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
            "w8_linear_invariant_kernel", "w8_linear_add_invariant", "w8_linear_swiglu_invariant",
            "w8_pack_bytes", "w8_pack", "w8_linear_invariant_packed", "w8_linear_invariant_packed_kernel",
+           "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed",
            "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32")
 
@@ -54,6 +55,8 @@ def _load():
     L.w8_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
     L.w8_pack.argtypes = [P, P, I64, I64, P, P, P]
     L.w8_linear_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
+    L.w8_linear_add_invariant_packed.argtypes = [P, P, P, P, I32, I32, P, I64, I64, I64, I64, I64, P]
+    L.w8_linear_swiglu_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
     L.w8_linear_invariant_packed_kernel.argtypes = [I64, I64, I32]
     L.w8_linear_invariant_packed_kernel.restype = ctypes.c_char_p
     L.vocab_block_logprob_workspace_bytes.argtypes = [I32, I64, I32]
@@ -66,7 +69,7 @@ def _load():
     L.w8i_exp32.argtypes = [P, P, I64, P]
     L.w8i_log32.argtypes = [P, P, I64, P]
     for name in ("w8_linear_add_invariant", "w8_linear_swiglu_invariant", "w8_pack_bytes", "w8_pack",
-                 "w8_linear_invariant_packed", "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
+                 "w8_linear_invariant_packed", "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed", "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -204,26 +207,58 @@ def w8_pack(W_q: torch.Tensor, scales: torch.Tensor) -> tuple[torch.Tensor, torc
     return Wp, Sp
 
 
-def w8_linear_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, t: int, T_pad: int, N: int,
-                               y: torch.Tensor | None = None) -> torch.Tensor:
-    """w8_linear_invariant over the packed layout from w8_pack (same bits).  x bf16 [>=t, K]; y bf16 [t, N]."""
+def _packed_args(Wp, Sp, x, t, N, rows, y, y_cols):
+    """Checks of a packed-layout call: Wp / Sp from w8_pack of a [rows, K] projection."""
     K = x.size(1)
-    wb, sb = w8_pack_bytes(N, K)
+    wb, sb = w8_pack_bytes(rows, K)
     if Wp.dtype != torch.int8 or Wp.numel() != wb or not Wp.is_contiguous():
-        raise ValueError("Wp must be the contiguous int8 output of w8_pack for this N and K")
+        raise ValueError("Wp must be the contiguous int8 output of w8_pack for this shape")
     if Sp.dtype not in (torch.int16, torch.float16) or Sp.numel() * 2 != sb or not Sp.is_contiguous():
-        raise ValueError("Sp must be the contiguous output of w8_pack for this N and K")
+        raise ValueError("Sp must be the contiguous output of w8_pack for this shape")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.size(0) < t:
         raise ValueError("x must be a bf16 [>=t, K] tensor")
     if y is None:
-        y = torch.empty((t, N), dtype=torch.bfloat16, device=Wp.device)
-    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != N or y.size(0) < t:
-        raise ValueError("y must be a bf16 [>=t, N] tensor")
+        y = torch.empty((t, y_cols), dtype=torch.bfloat16, device=Wp.device)
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != y_cols or y.size(0) < t:
+        raise ValueError(f"y must be a bf16 [>=t, {y_cols}] tensor")
     _same_gpu(("Wp", Wp), ("Sp", Sp), ("x", x), ("y", y))
+    return K, y
+
+
+def w8_linear_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, t: int, T_pad: int, N: int,
+                               y: torch.Tensor | None = None) -> torch.Tensor:
+    """w8_linear_invariant over the packed layout from w8_pack (same bits).  x bf16 [>=t, K]; y bf16 [t, N]."""
+    K, y = _packed_args(Wp, Sp, x, t, N, N, y, N)
     st = _lib.w8_linear_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y), int(N), K,
                                          _row_major(x, "x"), _row_major(y, "y"),
                                          ctypes.c_void_p(_stream(Wp.device)))
     _check("w8_linear_invariant_packed", st)
+    return y
+
+
+def w8_linear_add_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, residual: torch.Tensor,
+                                   t: int, T_pad: int, N: int, y: torch.Tensor | None = None) -> torch.Tensor:
+    """w8_linear_add_invariant over the packed layout (same bits); y may be `residual` itself."""
+    K, y = _packed_args(Wp, Sp, x, t, N, N, y, N)
+    _same_gpu(("Wp", Wp), ("residual", residual))
+    if residual.dtype != torch.bfloat16 or residual.dim() != 2 or residual.size(1) != N or residual.size(0) < t:
+        raise ValueError("residual must be a bf16 [>=t, N] tensor")
+    st = _lib.w8_linear_add_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), _ptr(residual), int(t), int(T_pad),
+                                             _ptr(y), int(N), K, _row_major(x, "x"),
+                                             _row_major(residual, "residual"), _row_major(y, "y"),
+                                             ctypes.c_void_p(_stream(Wp.device)))
+    _check("w8_linear_add_invariant_packed", st)
+    return y
+
+
+def w8_linear_swiglu_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, t: int, T_pad: int,
+                                      F: int, y: torch.Tensor | None = None) -> torch.Tensor:
+    """w8_linear_swiglu_invariant over the packed layout of the [2F, K] gate+up projection (same bits)."""
+    K, y = _packed_args(Wp, Sp, x, t, F, 2 * F, y, F)
+    st = _lib.w8_linear_swiglu_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y), int(F),
+                                                K, _row_major(x, "x"), _row_major(y, "y"),
+                                                ctypes.c_void_p(_stream(Wp.device)))
+    _check("w8_linear_swiglu_invariant_packed", st)
     return y
 
 

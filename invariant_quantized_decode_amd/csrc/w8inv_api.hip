@@ -107,34 +107,65 @@ const char* w8_linear_invariant_packed_kernel(int64_t N, int64_t K, int32_t T_pa
     return linear_packed_kernel_name(N, K, T_pad);
 }
 
-int w8_linear_add_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const uint16_t* residual,
-                            int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldr,
-                            int64_t ldy, void* stream) {
-    const int st = check_projection(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, N);
+// y is the residual itself (same pointer and stride), or the two do not overlap
+static bool residual_ok(const uint16_t* residual, const uint16_t* y, int32_t t, int64_t N, int64_t ldr, int64_t ldy) {
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(residual), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t r1 = r0 + (uintptr_t)(((int64_t)(t - 1) * ldr + N) * 2);
+    const uintptr_t y1 = y0 + (uintptr_t)(((int64_t)(t - 1) * ldy + N) * 2);
+    return (r0 == y0 && ldr == ldy) || r1 <= y0 || y1 <= r0;
+}
+
+static int linear_add(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* x, const uint16_t* residual,
+                      int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldr,
+                      int64_t ldy, void* stream) {
+    const int st = check_projection(W, S, x, t, T_pad, y, N, K, ldx, ldy, N);
     if (st != W8I_OK || t == 0) return st;
     if (!residual) return W8I_ENULL;
     if (ldr < N) return W8I_ESHAPE;
     if (!aligned(residual, 2)) return W8I_EALIGN;
-    // y is the residual itself, or the two do not overlap
-    const uintptr_t r0 = reinterpret_cast<uintptr_t>(residual), y0 = reinterpret_cast<uintptr_t>(y);
-    const uintptr_t r1 = r0 + (uintptr_t)(((int64_t)(t - 1) * ldr + N) * 2);
-    const uintptr_t y1 = y0 + (uintptr_t)(((int64_t)(t - 1) * ldy + N) * 2);
-    if (!(r0 == y0 && ldr == ldy) && r0 < y1 && y0 < r1) return W8I_ESHAPE;
-    return launch_linear_epilogue(kEpiAdd, W_q, scales, x, t, T_pad, y, N, K, ldx, ldy,
+    if (!residual_ok(residual, y, t, N, ldr, ldy)) return W8I_ESHAPE;
+    if (packed && packed_weight_bytes(N, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (packed && !aligned(S, 16)) return W8I_EALIGN;
+    return launch_linear_epilogue(kEpiAdd, packed, W, S, x, t, T_pad, y, N, K, ldx, ldy,
                                   LinearEpilogue{residual, ldr, 0}, as_stream(stream));
+}
+
+static int linear_swiglu(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* x, int32_t t,
+                         int32_t T_pad, uint16_t* y, int64_t F, int64_t K, int64_t ldx, int64_t ldy, void* stream) {
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
+    if (t < 0 || t > T_pad) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (F < 1 || F > kMaxDim) return W8I_ESHAPE;
+    const int st = check_projection(W, S, x, t, T_pad, y, 2 * F, K, ldx, ldy, F);
+    if (st != W8I_OK) return st;
+    if (packed && packed_weight_bytes(2 * F, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (packed && !aligned(S, 16)) return W8I_EALIGN;
+    return launch_linear_epilogue(kEpiSwiGLU, packed, W, S, x, t, T_pad, y, 2 * F, K, ldx, ldy,
+                                  LinearEpilogue{nullptr, 0, F}, as_stream(stream));
+}
+
+int w8_linear_add_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const uint16_t* residual,
+                            int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldr,
+                            int64_t ldy, void* stream) {
+    return linear_add(false, W_q, scales, x, residual, t, T_pad, y, N, K, ldx, ldr, ldy, stream);
+}
+
+int w8_linear_add_invariant_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* x, const uint16_t* residual,
+                                   int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t K, int64_t ldx,
+                                   int64_t ldr, int64_t ldy, void* stream) {
+    return linear_add(true, Wp, Sp, x, residual, t, T_pad, y, N, K, ldx, ldr, ldy, stream);
 }
 
 int w8_linear_swiglu_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, int32_t t,
                                int32_t T_pad, uint16_t* y, int64_t F, int64_t K, int64_t ldx, int64_t ldy,
                                void* stream) {
-    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
-    if (t < 0 || t > T_pad) return W8I_ET;
-    if (t == 0) return W8I_OK;
-    if (F < 1 || F > kMaxDim) return W8I_ESHAPE;
-    const int st = check_projection(W_q, scales, x, t, T_pad, y, 2 * F, K, ldx, ldy, F);
-    if (st != W8I_OK || t == 0) return st;
-    return launch_linear_epilogue(kEpiSwiGLU, W_q, scales, x, t, T_pad, y, 2 * F, K, ldx, ldy,
-                                  LinearEpilogue{nullptr, 0, F}, as_stream(stream));
+    return linear_swiglu(false, W_q, scales, x, t, T_pad, y, F, K, ldx, ldy, stream);
+}
+
+int w8_linear_swiglu_invariant_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* x, int32_t t,
+                                      int32_t T_pad, uint16_t* y, int64_t F, int64_t K, int64_t ldx, int64_t ldy,
+                                      void* stream) {
+    return linear_swiglu(true, Wp, Sp, x, t, T_pad, y, F, K, ldx, ldy, stream);
 }
 
 size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) {

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     constexpr int kXLoads = 4 * NT;                   // direct loads of 8 columns x 128 bytes per stage
     // weights + activations (+ scales)
     constexpr int kLoadsPerStage = 2 + kXLoads + (PK ? 1 : LS ? 0 : 2);
-    static_assert(!PK || (!LS && EPI == kEpiStore), "packed layout: scales per stage, plain store");
+    static_assert(!PK || !LS, "packed layout: scales come with each stage");
     static_assert(kScaleBytes > 0, "LDS");
     // one array per ring slot, so the compiler can wait for each slot's loads alone
     __shared__ __align__(16) unsigned char xr0[kSlotBytes];
@@ -214,10 +214,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         w_off[i] = (uint32_t)(row_of(16 * i + (lane & 15)) * K) + 16u * (lane >> 5);
         w_off_gs[i] = w_off[i] + 32u * ((lane >> 4) & 1);
     }
-    // packed: lane l takes bytes 16 l .. 16 l + 15 of each 1 KB block (row l % 32,
-    // K half l / 32 of the block's group) and the 4 bytes of its row's two scales
-    const uint32_t pk_w = (uint32_t)(blockIdx.x * P * 2048) + 16u * lane;
-    const uint32_t pk_s = (uint32_t)(blockIdx.x * P * 128) + 4u * (lane & 31);
+    // packed: lane (r, c) takes the 16 bytes of its row's K half c in each 1 KB
+    // half-block of its row's strip (for a plain strip: bytes 16 l .. 16 l + 15
+    // of the workgroup's own blocks), and the 4 bytes of its row's two scales
+    const int64_t pk_row = row_of(lane & 31);
+    const uint32_t pk_w = (uint32_t)((pk_row / kRows) * P * 2048) + 512u * (lane >> 5) + 16u * (uint32_t)(pk_row % kRows);
+    const uint32_t pk_s = (uint32_t)((pk_row / kRows) * P * 128) + 4u * (uint32_t)(pk_row % kRows);
     // direct load i of a stage: columns 8 i .. 8 i + 7 (sized for two tiles: an
     // array whose size depends on the template arguments, captured by the
     // lambdas below, made the host pass drop the kernel stubs)
@@ -860,13 +862,16 @@ int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X
     return launch_split<kEpiStore, true>(p, Wp, Sp, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
 }
 
-int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
-                           uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+int launch_linear_epilogue(int epi, bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
+                           int T_pad, uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                            hipStream_t stream) {
-    const LinearPlan p = plan_epilogue(epi, N, K, T_pad, S);
-    switch (epi) {
-        case kEpiAdd: return launch_split<kEpiAdd>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
-        case kEpiSwiGLU: return launch_split<kEpiSwiGLU>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+    const LinearPlan p = packed ? plan_split(T_pad / 16, 0) : plan_epilogue(epi, N, K, T_pad, S);
+    switch (epi * 2 + (packed ? 1 : 0)) {
+        case kEpiAdd * 2: return launch_split<kEpiAdd>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+        case kEpiAdd * 2 + 1: return launch_split<kEpiAdd, true>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+        case kEpiSwiGLU * 2: return launch_split<kEpiSwiGLU>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+        case kEpiSwiGLU * 2 + 1:
+            return launch_split<kEpiSwiGLU, true>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
         default: return W8I_ESHAPE;
     }
 }

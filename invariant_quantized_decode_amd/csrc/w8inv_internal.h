@@ -40,10 +40,11 @@ inline int64_t packed_weight_bytes(int64_t N, int64_t K) { return (N + 31) / 32 
 inline int64_t packed_scale_bytes(int64_t N, int64_t K) { return (N + 31) / 32 * ((K / kGroup + 1) / 2) * 128; }
 int launch_pack(const int8_t* W, const uint16_t* S, int64_t N, int64_t K, int8_t* Wp, uint16_t* Sp,
                 hipStream_t stream);
-// the projection with a fused epilogue (always the LDS-staged split kernel);
+// the projection with a fused epilogue (always the LDS-staged split kernel;
+// `packed`: W and S in the packed layout);
 // for kEpiSwiGLU, N is the projection's 2F rows and y has F columns
-int launch_linear_epilogue(int epi, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
-                           uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+int launch_linear_epilogue(int epi, bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
+                           int T_pad, uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                            hipStream_t stream);
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S);
 const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad);

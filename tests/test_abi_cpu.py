@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)

@@ -117,3 +117,27 @@ def test_fused_columns_are_t_invariant():
         ad = bits(w8.w8_linear_add_invariant(Wd, Sd, bf16(x[perm]), bf16(res[perm]), t, 32))
         assert np.array_equal(sw, full_sw[perm])
         assert np.array_equal(ad, full_add[perm])
+
+
+@pytest.mark.parametrize("N,K,t,T_pad", ADD)
+def test_packed_linear_add_gives_the_plain_bits(N, K, t, T_pad):
+    say(f"case packed linear_add N={N} K={K} t={t} T_pad={T_pad}")
+    rng, q, s, x = draw(N + K + t, N, K, T_pad)
+    res = synth.draw_acts(rng, T_pad, N)
+    Wd, Sd, Xd, Rd = i8(q), f16(s), bf16(x), bf16(res)
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    want = bits(w8.w8_linear_add_invariant(Wd, Sd, Xd, Rd, t, T_pad))
+    assert np.array_equal(bits(w8.w8_linear_add_invariant_packed(Wp, Sp, Xd, Rd, t, T_pad, N)), want)
+    Rw = Rd.clone()
+    w8.w8_linear_add_invariant_packed(Wp, Sp, Xd, Rw, t, T_pad, N, y=Rw)
+    assert np.array_equal(bits(Rw[:t]), want)
+
+
+@pytest.mark.parametrize("F,K,t,T_pad", SWIGLU + [(37, 1056, 5, 32)])  # F not a multiple of 16: strips straddled
+def test_packed_linear_swiglu_gives_the_plain_bits(F, K, t, T_pad):
+    say(f"case packed linear_swiglu F={F} K={K} t={t} T_pad={T_pad}")
+    rng, q, s, x = draw(F + K + t, 2 * F, K, T_pad)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    want = bits(w8.w8_linear_swiglu_invariant(Wd, Sd, Xd, t, T_pad))
+    assert np.array_equal(bits(w8.w8_linear_swiglu_invariant_packed(Wp, Sp, Xd, t, T_pad, F)), want)
