@@ -389,22 +389,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     }
 
     // Left fold of the 8 slice sums, ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7,
-    // shared by the waves: every slice sum goes to ring slots 0 and 1
-    // (NT * 8 KB per wave, four waves per slot), then wave w folds and stores
-    // values V = w, w + 8, ... (V = 16 tt + v) of every lane.  The barrier's
-    // fence also waits for the prefetches past the slice ends, which still
-    // write into the ring.
-    __syncthreads();
-    auto part_of = [&](int w) {
-        return reinterpret_cast<double*>((w < 4 ? xr0 : xr1) + (w & 3) * (NT * 16 * 64 * 8));
+    // shared by the waves.  Each wave waits for its own loads (the prefetches
+    // past its slice's end still write into its ring regions), then writes its
+    // slice sum into its own regions of ring slots 0 and 1 (values 16 tt + v,
+    // the first NT * 8 in slot 0, the rest in slot 1), so only one barrier
+    // stands between the last wave's finish and the fold; then wave w folds
+    // and stores values V = w, w + 8, ... (V = 16 tt + v) of every lane.
+    wait_vm<0>();
+    auto part = [&](int w, int V) {
+        constexpr int kHalf = NT * 8;
+        return reinterpret_cast<double*>((V < kHalf ? xr0 : xr1) + w * kStageBytes) + (V % kHalf) * 64 + lane;
     };
-    {
-        double* f = part_of(wave);
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) f[(tt * 16 + v) * 64 + lane] = acc[tt][v];
-    }
+        for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) *part(wave, tt * 16 + v) = acc[tt][v];
     __syncthreads();
     const int64_t n = n0 + r;
 #pragma unroll
@@ -412,9 +411,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         const int V = wave + kKSlices * k;
         const int tt = V >> 4, v = V & 15;
         if (v >= ((tt == NT - 1) ? kLastValues : 16)) continue;
-        double sum = part_of(0)[V * 64 + lane];
+        double sum = *part(0, V);
 #pragma unroll
-        for (int w = 1; w < kKSlices; ++w) sum = sum + part_of(w)[V * 64 + lane];
+        for (int w = 1; w < kKSlices; ++w) sum = sum + *part(w, V);
         // MFMA 32x32 result layout: lane holds column (= weight row) lane % 32
         // and rows 8*(v/4) + 4*(lane/32) + v%4 (= activation columns) of tile tt
         const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
