@@ -796,16 +796,31 @@ const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
     }
 }
 
+// Packed layout (scales come with each stage, no LDS for them): the split
+// kernel's ring is the only LDS, so with one 32-column tile and a ring of two
+// stages (64 KB) two workgroups fit on a CU, one streaming while the other
+// starts or folds.  That pays once there are workgroups to spare (at least two
+// per CU: 512 row groups of 32); below it the deeper ring of three is faster.
+constexpr int64_t kPackedTwoPerCuRows = 512 * 32;
+
+static LinearPlan plan_packed(int tp16, int64_t row_groups) {
+    LinearPlan p = plan_split(tp16, 0);
+    if ((tp16 + 1) / 2 == 1 && row_groups * kRows >= kPackedTwoPerCuRows) p.depth = 2;
+    return p;
+}
+
 const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad) {
     static const char* const tiles[2] = {"gemm_w8g32_tiles<1, false, true>", "gemm_w8g32_tiles<2, false, true>"};
-    static const char* const split[4] = {
-        "gemm_w8g32_split_lds<1, 3, false, 0, true>", "gemm_w8g32_split_lds<2, 3, false, 0, true>",
-        "gemm_w8g32_split_lds<3, 2, false, 0, true>", "gemm_w8g32_split_lds<4, 2, false, 0, true>"};
+    static const char* const split[4][2] = {
+        {"gemm_w8g32_split_lds<1, 2, false, 0, true>", "gemm_w8g32_split_lds<1, 3, false, 0, true>"},
+        {"gemm_w8g32_split_lds<2, 2, false, 0, true>", "gemm_w8g32_split_lds<2, 3, false, 0, true>"},
+        {"gemm_w8g32_split_lds<3, 2, false, 0, true>", ""},
+        {"gemm_w8g32_split_lds<4, 2, false, 0, true>", ""}};
     (void)K;
     if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return "";
     if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256) return tiles[T_pad / 16 - 1];
-    const LinearPlan p = plan_split(T_pad / 16, 0);
-    return p.depth == (T_pad <= 32 ? 3 : 2) ? split[T_pad / 16 - 1] : "";
+    const LinearPlan p = plan_packed(T_pad / 16, (N + kRows - 1) / kRows);
+    return split[T_pad / 16 - 1][p.depth - 2];
 }
 
 template <int EPI, bool PK = false>
@@ -830,6 +845,8 @@ static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S,
         W8I_SPLIT_LAUNCH(4, 2, true)
         W8I_SPLIT_LAUNCH(1, 3, false)
         W8I_SPLIT_LAUNCH(2, 3, false)
+        W8I_SPLIT_LAUNCH(1, 2, false)
+        W8I_SPLIT_LAUNCH(2, 2, false)
         W8I_SPLIT_LAUNCH(3, 2, false)
         W8I_SPLIT_LAUNCH(4, 2, false)
         default:
@@ -857,14 +874,16 @@ int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X
     // the persistent kernel where it runs the plain layout, else the split kernel
     if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256)
         return launch_tiles(Wp, Sp, X, t, T_pad, Y, N, K, ldx, ldy, 2, stream);
-    const LinearPlan p = plan_split(T_pad / 16, 0);  // scales come with each stage
+    const LinearPlan p = plan_packed(T_pad / 16, (N + kRows - 1) / kRows);
     return launch_split<kEpiStore, true>(p, Wp, Sp, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
 }
 
 int launch_linear_epilogue(int epi, bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
                            int T_pad, uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                            hipStream_t stream) {
-    const LinearPlan p = packed ? plan_split(T_pad / 16, 0) : plan_epilogue(epi, N, K, T_pad, S);
+    // (SwiGLU: a workgroup covers 16 gate and 16 up rows, one row group of 32)
+    const LinearPlan p = packed ? plan_packed(T_pad / 16, epi == kEpiSwiGLU ? (N / 2 + 15) / 16 : (N + kRows - 1) / kRows)
+                                : plan_epilogue(epi, N, K, T_pad, S);
     switch (epi * 2 + (packed ? 1 : 0)) {
         case kEpiAdd * 2: return launch_split<kEpiAdd>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
         case kEpiAdd * 2 + 1: return launch_split<kEpiAdd, true>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);

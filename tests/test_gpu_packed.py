@@ -62,6 +62,8 @@ CASES = [  # N, K, T_pad: headline shape, ragged rows, odd K/32, empty slices, e
     (40, 17408, 64),
     (24, 36896, 16),
     (5120, 6144, 32),
+    (16400, 1056, 32),   # >= 16384 rows: two workgroups per CU (ring of two stages)
+    (16384, 2080, 16),
 ]
 
 
