@@ -48,7 +48,8 @@ def lib():
         P, I64, U32, F32, F64, I32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
                                       ctypes.c_float, ctypes.c_double, ctypes.c_int)
         L.oracle_w8_linear.argtypes = [P, P, P, I64, I64, I64, I64, P, I64, P]
-        L.oracle_block_logprob.argtypes = [P, P, I64, I64, I64, I64, P, P]
+        L.oracle_block_logprob.argtypes = [P, P, I64, I64, I64, I64, P, P, I32]
+        L.oracle_argmax.argtypes = [P, I64, I64, I64, P]
         L.oracle_logprob_ref.argtypes = [P, P, I64, I64, I64, P]
         L.oracle_exp32.argtypes, L.oracle_exp32.restype = [F32], F32
         L.oracle_log32.argtypes, L.oracle_log32.restype = [F32], F32
@@ -98,8 +99,11 @@ def w8_linear(q, s, x, rows=None) -> np.ndarray:
     return y
 
 
-def block_logprob(logits, targets, block: int, return_partials: bool = False):
-    """Fixed-order fp32 target logprob over `block`-wide vocabulary blocks; fp32 [t]."""
+def block_logprob(logits, targets, block: int, return_partials: bool = False, direct: bool = False):
+    """Fixed-order fp32 target logprob over `block`-wide vocabulary blocks; fp32 [t].
+
+    direct=False: the blockwise form -(log(sum_exp) - target); True: blockwise-direct,
+    target - log(sum_exp) (tokenspeed numerics, "Logprobs")."""
     logits = _c(logits, np.uint16)
     targets = _c(targets, np.int64)
     t, V = logits.shape
@@ -108,8 +112,19 @@ def block_logprob(logits, targets, block: int, return_partials: bool = False):
     part = np.empty((t, nb), dtype=np.float32) if return_partials else None
     if t:
         lib().oracle_block_logprob(_ptr(logits), _ptr(targets), block, t, V, V, _ptr(out),
-                                   _ptr(part) if part is not None else None)
+                                   _ptr(part) if part is not None else None, 1 if direct else 0)
     return (out, part) if return_partials else out
+
+
+def argmax(logits) -> np.ndarray:
+    """Canonical greedy argmax per column: the maximum, lowest index on ties, +-0 equal, the first
+    NaN when there is one (tokenspeed numerics, "Logprobs"); int64 [t]."""
+    logits = _c(logits, np.uint16)
+    t, V = logits.shape
+    out = np.empty(t, dtype=np.int64)
+    if t:
+        lib().oracle_argmax(_ptr(logits), t, V, V, _ptr(out))
+    return out
 
 
 def logprob_ref(logits, targets) -> np.ndarray:

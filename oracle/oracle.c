@@ -182,7 +182,7 @@ static float tree_sum(const float *e, int64_t w) {
  * When partials != NULL the block partials are also written, [t, nb]. */
 void oracle_block_logprob(const uint16_t *logits, const int64_t *targets,
                           int64_t block, int64_t t, int64_t V, int64_t ldl,
-                          float *out, float *partials) {
+                          float *out, float *partials, int direct) {
     const int64_t nb = (V + block - 1) / block;
 #pragma omp parallel
     {
@@ -215,8 +215,14 @@ void oracle_block_logprob(const uint16_t *logits, const int64_t *targets,
             }
             float Lg = oracle_log32(S);
             float st = bf16_as_float(l[tg]) - m;
-            float d = Lg - st;
-            out[j] = -d;
+            /* blockwise: -(Lg - st), -0.0 for a certain token; blockwise-direct:
+             * st - Lg, +0.0 for it (tokenspeed numerics, "Logprobs") */
+            if (direct) {
+                out[j] = st - Lg;
+            } else {
+                float d = Lg - st;
+                out[j] = -d;
+            }
         }
         free(e);
     }
@@ -287,4 +293,28 @@ void oracle_add(const uint16_t *a, const uint16_t *b, int64_t t, int64_t H,
     for (int64_t j = 0; j < t; ++j)
         for (int64_t h = 0; h < H; ++h)
             y[j * H + h] = (double)bf16_as_float(a[j * lda + h]) + (double)bf16_as_float(b[j * ldb + h]);
+}
+
+/* Canonical greedy argmax of each column (tokenspeed numerics, "Logprobs":
+ * the vocabulary-parallel argmax takes the maximum and, among equal values,
+ * the lowest index; signed zeros count as equal).  Reading for NaN (the page
+ * is silent): a NaN counts as larger than every number, and among NaNs the
+ * lowest index wins -- what torch.argmax and numpy.argmax do.  A plain scan in
+ * index order that moves only on a strictly larger value. */
+void oracle_argmax(const uint16_t *logits, int64_t t, int64_t V, int64_t ldl, int64_t *out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < t; ++j) {
+        const uint16_t *l = logits + j * ldl;
+        int64_t best = 0;
+        float bv = bf16_as_float(l[0]);
+        for (int64_t v = 1; v < V; ++v) {
+            const float lv = bf16_as_float(l[v]);
+            if (isnan(bv)) break;                  /* the first NaN is the answer */
+            if (isnan(lv) || lv > bv) {
+                best = v;
+                bv = lv;
+            }
+        }
+        out[j] = best;
+    }
 }

@@ -209,3 +209,70 @@ def test_shift_uses_the_global_row_max():
     assert part[0, 0] == exp_rn32(-3.0) and part[0, 1] == 1.0
     S = np.float32(part[0, 0]) + np.float32(1.0)
     assert out[0] == -(ln_rn32(float(S)) - np.float32(-3.0))
+
+
+# ------------------------------------------------------------- blockwise-direct
+def test_direct_form_gives_plus_zero_and_the_same_nonzero_values():
+    """tokenspeed numerics, "Logprobs": blockwise-direct is target - log(sum_exp) over the same
+    reduction.  A certain token gives +0.0 (blockwise: -0.0); any other result equals the
+    blockwise value, because IEEE subtraction is exactly sign-symmetric (a - b = -(b - a))."""
+    V, block = 10000, 256
+    row = np.full(V, bf16(-150.0), dtype=np.uint16)
+    row[4321] = bf16(2.5)
+    row[17] = bf16(-90.0)
+    logits = np.stack([row, row, row])
+    tg = np.array([4321, 17, 9999], dtype=np.int64)
+    d = oracle.block_logprob(logits, tg, block, direct=True)
+    assert d[0] == 0 and math.copysign(1.0, d[0]) > 0        # certain token: +0.0
+    assert d[1] == np.float32(-92.5) and d[2] == np.float32(-152.5)
+    rng = np.random.default_rng(3)
+    lg = synth.f32_to_bf16_bits((rng.standard_normal((4, 3000)) * 8).astype(np.float32))
+    tg = rng.integers(0, 3000, 4)
+    a = oracle.block_logprob(lg, tg, 512)
+    b = oracle.block_logprob(lg, tg, 512, direct=True)
+    assert np.all(a != 0) and np.array_equal(f32_bits(b), f32_bits(a))
+    u = oracle.block_logprob(np.full((1, 248320), bf16(3.0), dtype=np.uint16), np.array([7]), 4096, direct=True)
+    assert u[0] == -ln_rn32(248320)
+
+
+# ---------------------------------------------------------------- greedy argmax
+def _argmax_by_hand(row_bits):
+    """The rule written out: scan in index order; a NaN is larger than any number and the first
+    NaN wins; otherwise move only to a strictly larger value (ties keep the lowest index;
+    -0 == +0)."""
+    vals = [float(synth.bf16_bits_to_f32(np.array([b], dtype=np.uint16))[0]) for b in row_bits]
+    best = 0
+    for i, v in enumerate(vals):
+        if math.isnan(vals[best]):
+            break
+        if math.isnan(v) or v > vals[best]:
+            best = i
+    return best
+
+
+def test_argmax_hand_cases():
+    rows = [
+        [bf16(1.0), bf16(2.0), bf16(2.0), bf16(-3.0)],                # tie: lowest index
+        [0x8000, 0x0000, 0x8000, bf16(-1.0)],                        # -0 / +0 tie: index 0
+        [bf16(-1.0), 0x0000, 0x8000, bf16(-2.0)],                     # +0 before -0: index 1
+        [bf16(5.0), 0x7FC0, bf16(9.0), 0xFFC1],                       # first NaN wins (even over larger numbers)
+        [0xFF80, 0xFF80, 0xFF80, 0xFF80],                             # all -inf: index 0
+        [bf16(1.0), 0x7F80, bf16(3.0), 0x7F80],                       # +inf, first one
+    ]
+    want = [1, 0, 1, 1, 0, 1]
+    got = oracle.argmax(np.array(rows, dtype=np.uint16))
+    assert got.tolist() == want
+
+
+def test_argmax_matches_the_rule_and_numpy():
+    """Brute force of the written-out rule on rows full of exact ties, signed zeros, infinities
+    and NaNs; on rows without NaN it is numpy's argmax of the fp32 values (first maximum)."""
+    rng = np.random.default_rng(11)
+    pool = np.array([bf16(v) for v in (-2.0, -1.0, -0.5, 0.5, 1.0, 3.0)] + [0x0000, 0x8000, 0x7F80, 0xFF80],
+                    dtype=np.uint16)
+    rows = pool[rng.integers(0, len(pool), (300, 37))]
+    rows[::7, rng.integers(0, 37)] = 0x7FC1   # NaN in some rows
+    got = oracle.argmax(rows)
+    assert got.tolist() == [_argmax_by_hand(r) for r in rows]
+    clean = ~np.isnan(synth.bf16_bits_to_f32(rows)).any(axis=1)
+    assert np.array_equal(got[clean], np.argmax(synth.bf16_bits_to_f32(rows[clean]), axis=1))

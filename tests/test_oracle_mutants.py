@@ -39,6 +39,9 @@ MUTANTS = {
         " float lu = bf16_as_float(l[u]); if (lu > bm) bm = lu; } float shifted = bf16_as_float(l[v]) - bm;"),
     "padding not exactly zero": ("e[v] = 0.0f;", "e[v] = 1e-30f;"),
     "positive-zero (direct) form": ("out[j] = -d;", "out[j] = st - Lg;"),
+    "direct form with the blockwise sign": ("out[j] = st - Lg;", "out[j] = -(Lg - st);"),
+    "argmax ties take the last index": ("if (isnan(lv) || lv > bv) {", "if (isnan(lv) || lv >= bv) {"),
+    "argmax skips NaN": ("if (isnan(lv) || lv > bv) {", "if (lv > bv) {"),
     "bf16 rounding truncates": ("double r = nearbyint(a / ulp) * ulp;", "double r = floor(a / ulp) * ulp;"),
     "exp32 through fp32 libm": (
         "float oracle_exp32(float x) { return (float)expl((long double)x); }",
