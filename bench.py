@@ -405,6 +405,40 @@ def run_all(torch, w8, synth, dev, args):
                           "t": t, "us": round(sec * 1e6, 2), "alg_gbs": round(alg / sec / 1e9, 1),
                           "roofline_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
                           "cpu_oracle_us": round(csec * 1e6, 1)}), flush=True)
+        # the other head epilogues on the same logits: canonical greedy argmax (one pass over the
+        # logits) and the blockwise-direct logprob form
+        aws = torch.empty(max(16, w8.vocab_argmax_workspace_bytes(t, V)), dtype=torch.uint8, device=dev)
+        aout = torch.empty(t, dtype=torch.int64, device=dev)
+        for ename, efn, ebytes, okind in (
+                ("greedy argmax", lambda: w8.vocab_argmax(logits, out=aout, workspace=aws), 2 * t * V, "argmax"),
+                ("block logprob, blockwise-direct",
+                 lambda: w8.vocab_block_logprob_direct(logits, targets, block, out=out, workspace=ws), alg, "direct")):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                efn()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=stream):
+                    for _ in range(20):
+                        efn()
+                graph.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(50):
+                    graph.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 1e3 / 1000
+            c0 = time.perf_counter()
+            if okind == "argmax":
+                oracle.argmax(lh)
+            else:
+                oracle.block_logprob(lh, targets.cpu().numpy(), block, direct=True)
+            csec = time.perf_counter() - c0
+            print(json.dumps({"workload": f"vocab {ename} V={V}", "t": t, "us": round(sec * 1e6, 2),
+                              "alg_gbs": round(ebytes / sec / 1e9, 1),
+                              "roofline_frac": round(ebytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                              "cpu_oracle_us": round(csec * 1e6, 1)}), flush=True)
 
 
 if __name__ == "__main__":

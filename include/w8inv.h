@@ -232,6 +232,40 @@ int vocab_block_logprob(const uint16_t *logits, const int64_t *targets, int32_t 
                         float *out, int32_t t, int64_t V, int64_t ldl,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* The blockwise-direct form (tokenspeed numerics, "Logprobs": target -
+ * log(sum_exp) for trainers that need +0.0): the same reduction, the last step
+ * out = s_t - LOG32(S) in fp32, so out is +0.0 for a certain token and equals
+ * vocab_block_logprob's value wherever that is not zero.  Arguments, workspace
+ * and errors as for vocab_block_logprob. */
+int vocab_block_logprob_direct(const uint16_t *logits, const int64_t *targets, int32_t block,
+                               float *out, int32_t t, int64_t V, int64_t ldl,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Canonical greedy argmax of each column (LM-head epilogue).
+ *
+ * Source: tokenspeed numerics, "Logprobs" section: the vocabulary-parallel
+ * argmax reduces (maximum, global index) keys with MAX so that ties select the
+ * lowest index, with one key for both signed zeros; the ninfer issue's
+ * sampling row asks for the canonical lowest-index argmax because exact logit
+ * ties happen.  A NaN counts as larger than every number, and the lowest-index
+ * NaN wins (the pages are silent; this is what torch and numpy do).
+ *
+ *   out[j] = the lowest v < V with l_v = max_u l_u (or the lowest NaN index)
+ *
+ *   logits bf16 [t, ldl] row-major, 2-byte aligned, ldl >= V, 1 <= V <= 2^31
+ *          (16-byte rows select 128-bit loads; the result is the same).
+ *   out    int64 [t], 8-byte aligned.
+ *   workspace device buffer of at least vocab_argmax_workspace_bytes(t, V)
+ *          bytes, 8-byte aligned; contents are scratch.
+ * Integer keys only: the result is exact and independent of t, of the other
+ * columns and of the order of any reduction.
+ * ------------------------------------------------------------------------- */
+size_t vocab_argmax_workspace_bytes(int32_t t, int64_t V);
+
+int vocab_argmax(const uint16_t *logits, int64_t *out, int32_t t, int64_t V, int64_t ldl,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Column-local glue between the projections of one decode layer.  The ninfer
  * issue's "Where t selects arithmetic" notes that norms and other per-lane

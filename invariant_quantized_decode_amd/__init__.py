@@ -28,7 +28,8 @@ EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_by
            "w8_linear_invariant_kernel", "w8_linear_add_invariant", "w8_linear_swiglu_invariant",
            "w8_pack_bytes", "w8_pack", "w8_linear_invariant_packed", "w8_linear_invariant_packed_kernel",
            "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed",
-           "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "w8i_rmsnorm", "w8i_swiglu",
+           "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "vocab_block_logprob_direct",
+           "vocab_argmax_workspace_bytes", "vocab_argmax", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32")
 
 
@@ -63,6 +64,10 @@ def _load():
     L.vocab_block_logprob_workspace_bytes.restype = SZ
     L.vocab_block_logprob.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
     L.vocab_block_logprob.restype = ctypes.c_int
+    L.vocab_block_logprob_direct.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
+    L.vocab_block_logprob_direct.restype = ctypes.c_int
+    L.vocab_argmax_workspace_bytes.argtypes, L.vocab_argmax_workspace_bytes.restype = [I32, I64], SZ
+    L.vocab_argmax.argtypes, L.vocab_argmax.restype = [P, P, I32, I64, I64, P, SZ, P], ctypes.c_int
     L.w8i_rmsnorm.argtypes = [P, P, F32, P, I32, I64, I64, I64, P]
     L.w8i_swiglu.argtypes = [P, P, I32, I64, I64, I64, P]
     L.w8i_residual_add.argtypes = [P, P, P, I32, I64, I64, I64, I64, P]
@@ -279,8 +284,10 @@ def vocab_block_logprob_workspace_bytes(t: int, V: int, block: int) -> int:
 
 
 def vocab_block_logprob(logits: torch.Tensor, targets: torch.Tensor, block: int, out: torch.Tensor | None = None,
-                        t: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """fp32 [t] target logprobs by `block`-wide vocabulary blocks.  logits bf16 [t, V] (rows contiguous)."""
+                        t: int | None = None, workspace: torch.Tensor | None = None,
+                        direct: bool = False) -> torch.Tensor:
+    """fp32 [t] target logprobs by `block`-wide vocabulary blocks.  logits bf16 [t, V] (rows contiguous).
+    direct=True calls vocab_block_logprob_direct (the +0.0 form)."""
     if logits.dtype != torch.bfloat16 or logits.dim() != 2:
         raise ValueError("logits must be a bf16 [t, V] tensor")
     t = logits.size(0) if t is None else int(t)
@@ -299,9 +306,45 @@ def vocab_block_logprob(logits: torch.Tensor, targets: torch.Tensor, block: int,
     _same_gpu(("logits", logits), ("targets", targets), ("out", out), ("workspace", workspace))
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
-    st = _lib.vocab_block_logprob(_ptr(logits), _ptr(targets), int(block), _ptr(out), t, V, ldl, _ptr(workspace),
-                                  workspace.numel(), ctypes.c_void_p(_stream(logits.device)))
-    _check("vocab_block_logprob", st)
+    fn = _lib.vocab_block_logprob_direct if direct else _lib.vocab_block_logprob
+    st = fn(_ptr(logits), _ptr(targets), int(block), _ptr(out), t, V, ldl, _ptr(workspace), workspace.numel(),
+            ctypes.c_void_p(_stream(logits.device)))
+    _check("vocab_block_logprob_direct" if direct else "vocab_block_logprob", st)
+    return out
+
+
+def vocab_block_logprob_direct(logits: torch.Tensor, targets: torch.Tensor, block: int, **kw) -> torch.Tensor:
+    """The blockwise-direct form, target - log(sum_exp): +0.0 for a certain token."""
+    return vocab_block_logprob(logits, targets, block, direct=True, **kw)
+
+
+def vocab_argmax_workspace_bytes(t: int, V: int) -> int:
+    return int(_lib.vocab_argmax_workspace_bytes(int(t), int(V)))
+
+
+def vocab_argmax(logits: torch.Tensor, out: torch.Tensor | None = None, t: int | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """int64 [t]: each column's canonical greedy argmax (lowest index among equal maxima, +-0 equal,
+    the first NaN if any).  logits bf16 [t, V] (rows contiguous)."""
+    if logits.dtype != torch.bfloat16 or logits.dim() != 2:
+        raise ValueError("logits must be a bf16 [t, V] tensor")
+    t = logits.size(0) if t is None else int(t)
+    V = logits.size(1)
+    ldl = _row_major(logits, "logits")
+    if out is None:
+        out = torch.empty(t, dtype=torch.int64, device=logits.device)
+    _dtype(out, "out", torch.int64)
+    if out.numel() < t or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int64 [t] tensor")
+    need = vocab_argmax_workspace_bytes(t, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    _same_gpu(("logits", logits), ("out", out), ("workspace", workspace))
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    st = _lib.vocab_argmax(_ptr(logits), _ptr(out), t, V, ldl, _ptr(workspace), workspace.numel(),
+                           ctypes.c_void_p(_stream(logits.device)))
+    _check("vocab_argmax", st)
     return out
 
 

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw8inv.so")
 
-SOURCES = ["w8inv_api.hip", "w8inv_gemm.hip", "w8inv_logprob.hip", "w8inv_glue.hip", "w8inv_pack.hip"]
+SOURCES = ["w8inv_api.hip", "w8inv_gemm.hip", "w8inv_logprob.hip", "w8inv_glue.hip", "w8inv_pack.hip",
+           "w8inv_argmax.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -173,8 +173,8 @@ size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) 
     return logprob_workspace_bytes(t, V, block);
 }
 
-int vocab_block_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
-                        int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, void* stream) {
+static int block_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
+                         int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, bool direct, void* stream) {
     if (block < 256 || block > 32768 || (block & (block - 1)) != 0) return W8I_EBLOCK;
     if (t < 0 || t > 65535) return W8I_ET;
     if (t == 0) return W8I_OK;
@@ -184,7 +184,34 @@ int vocab_block_logprob(const uint16_t* logits, const int64_t* targets, int32_t 
     if (!aligned(logits, 2) || !aligned(targets, 8) || !aligned(out, 4)) return W8I_EALIGN;
     if (!workspace || workspace_bytes < logprob_workspace_bytes(t, V, block)) return W8I_EWORKSPACE;
     if (!aligned(workspace, 16)) return W8I_EALIGN;
-    return launch_logprob(logits, targets, block, out, t, V, ldl, workspace, as_stream(stream));
+    return launch_logprob(logits, targets, block, out, t, V, ldl, workspace, direct, as_stream(stream));
+}
+
+int vocab_block_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
+                        int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, void* stream) {
+    return block_logprob(logits, targets, block, out, t, V, ldl, workspace, workspace_bytes, false, stream);
+}
+
+int vocab_block_logprob_direct(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
+                               int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, void* stream) {
+    return block_logprob(logits, targets, block, out, t, V, ldl, workspace, workspace_bytes, true, stream);
+}
+
+size_t vocab_argmax_workspace_bytes(int32_t t, int64_t V) {
+    if (t <= 0 || V <= 0 || V > ((int64_t)1 << 31)) return 0;
+    return argmax_workspace_bytes(t, V);
+}
+
+int vocab_argmax(const uint16_t* logits, int64_t* out, int32_t t, int64_t V, int64_t ldl, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (t < 0 || t > 65535) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!logits || !out) return W8I_ENULL;
+    if (V < 1 || V > ((int64_t)1 << 31) || ldl < V || ldl > kMaxDim) return W8I_ESHAPE;
+    if (!aligned(logits, 2) || !aligned(out, 8)) return W8I_EALIGN;
+    if (!workspace || workspace_bytes < argmax_workspace_bytes(t, V)) return W8I_EWORKSPACE;
+    if (!aligned(workspace, 8)) return W8I_EALIGN;
+    return launch_argmax(logits, out, t, V, ldl, workspace, as_stream(stream));
 }
 
 int w8i_rmsnorm(const uint16_t* x, const uint16_t* weight, float eps, uint16_t* y, int32_t t, int64_t H, int64_t ldx,

@@ -51,7 +51,11 @@ const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad);
 
 size_t logprob_workspace_bytes(int t, int64_t V, int block);
 int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,
-                   int64_t ldl, void* ws, hipStream_t stream);
+                   int64_t ldl, void* ws, bool direct, hipStream_t stream);
+
+constexpr int kArgmaxBlock = 4096;  // vocabulary entries per workgroup of the argmax's first pass
+size_t argmax_workspace_bytes(int t, int64_t V);
+int launch_argmax(const uint16_t* L, int64_t* out, int t, int64_t V, int64_t ldl, void* ws, hipStream_t stream);
 
 int launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int t, int64_t H, int64_t ldx,
                    int64_t ldy, hipStream_t stream);

@@ -190,6 +190,9 @@ __global__ __launch_bounds__(kLpThreads) void lp_block_sumexp(const uint16_t* __
 // One wave per column: the block partials are staged in LDS by all lanes
 // (their loads in flight together), then lane 0 folds them left to right.
 constexpr int kFoldChunk = 1024;  // partials staged per pass
+// DIRECT: the blockwise-direct form st - Lg (+0.0 for a certain token) instead
+// of the blockwise -(Lg - st) (-0.0); tokenspeed numerics, "Logprobs".
+template <bool DIRECT>
 __global__ __launch_bounds__(64) void lp_fold(const uint16_t* __restrict__ L, int64_t V, int64_t ldl,
                                                const int64_t* __restrict__ targets, int nb,
                                                const float* __restrict__ M, const float* __restrict__ P,
@@ -227,8 +230,12 @@ __global__ __launch_bounds__(64) void lp_fold(const uint16_t* __restrict__ L, in
     }
     const float Lg = log32(S);
     const float st = bf16_to_f32(L[(int64_t)j * ldl + tg]) - m;
-    const float d = Lg - st;
-    out[j] = -d;
+    if constexpr (DIRECT) {
+        out[j] = st - Lg;
+    } else {
+        const float d = Lg - st;
+        out[j] = -d;
+    }
 }
 
 static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -254,7 +261,7 @@ static void launch_lp_e(const uint16_t* L, int64_t V, int64_t ldl, int nb, int t
 }
 
 int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V, int64_t ldl,
-                   void* ws, hipStream_t stream) {
+                   void* ws, bool direct, hipStream_t stream) {
     const int64_t nb = (V + block - 1) / block;
     float* M = static_cast<float*>(ws);
     float* P = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -271,7 +278,10 @@ int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* 
         case 128: launch_lp_e<128>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
         default: return W8I_EBLOCK;
     }
-    hipLaunchKernelGGL(lp_fold, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
+    if (direct)
+        hipLaunchKernelGGL(lp_fold<true>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
+    else
+        hipLaunchKernelGGL(lp_fold<false>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 

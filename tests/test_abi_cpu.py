@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -156,6 +156,22 @@ def logprob(Lg=A, T=A, block=4096, out=A, t=4, V=248320, ldl=248320, ws=A, wsb=1
 ])
 def test_logprob_rejects_invalid_arguments(kw, code):
     assert logprob(**kw) == code
+
+
+def test_direct_and_argmax_validation():
+    assert L.vocab_block_logprob_direct(fake(A), fake(A), 1000, fake(A), 4, 248320, 248320, fake(A), 1 << 20,
+                                        None) == -5
+    assert L.vocab_block_logprob_direct(fake(A), fake(A), 4096, fake(A), 4, 248320, 248320, fake(A), 100, None) == -6
+    f = L.vocab_argmax
+    need = L.vocab_argmax_workspace_bytes(32, 248320)
+    assert need == 32 * 61 * 8
+    assert f(fake(A), fake(A), 0, 248320, 248320, None, 0, None) == 0
+    assert f(None, fake(A), 4, 248320, 248320, fake(A), need, None) == -1
+    assert f(fake(A), fake(A + 4), 4, 248320, 248320, fake(A), need, None) == -3
+    assert f(fake(A), fake(A), 4, 248320, 1000, fake(A), need, None) == -2
+    assert f(fake(A), fake(A), 4, (1 << 31) + 1, (1 << 31) + 1, fake(A), 1 << 30, None) == -2
+    assert f(fake(A), fake(A), 4, 248320, 248320, fake(A), 10, None) == -6
+    assert f(fake(A), fake(A), 4, 248320, 248320, fake(A + 4), need, None) == -3
 
 
 def test_logprob_workspace_size():
