@@ -77,10 +77,11 @@ const char *w8i_version(void);
  *   - int8 codes become bf16 exactly; each 32-element group's products are
  *     summed by bf16 matrix-core instructions into fp32 starting from zero;
  *   - that group sum is multiplied by its fp16 scale and accumulated in fp64;
- *   - K is cut into 8 contiguous slices of whole pairs of groups: with
- *     G = K/32 groups and P = floor(G/2) pairs, slice i covers groups
- *     [2*floor(P*i/8), 2*floor(P*(i+1)/8)) and, when G is odd, slice 7 also
- *     takes the last group.  Each slice is summed in ascending group order
+ *   - K is cut into 8 contiguous slices of whole pairs of groups, slices
+ *     0..3 twice as long as slices 4..7: with G = K/32 groups, P = floor(G/2)
+ *     pairs and c = (0, 2, 4, 6, 8, 9, 10, 11, 12), slice i covers groups
+ *     [2*floor(P*c_i/12), 2*floor(P*c_{i+1}/12)) and, when G is odd, slice 7
+ *     also takes the last group.  Each slice is summed in ascending group order
  *     (an empty slice is +0) and the 8 slice sums are combined by the left
  *     fold ((((((s0+s1)+s2)+s3)+s4)+s5)+s6)+s7.  The plan depends on K only;
  *   - the fp64 result is rounded once to bf16, nearest-even.
