@@ -116,3 +116,36 @@ def test_decode_chain_lanes_are_composition_independent():
     final = synth.bf16_bits_to_f32(bits(states))
     say(f"case chain: all lanes bitwise identical alone; final |h| max {float(np.abs(final).max()):.3g}")
     assert np.isfinite(final).all()
+
+
+def fast_layer(h, P):
+    """The same layer on the fast path: packed weights (w8_pack) and the fused epilogues
+    (O + residual, gate+up + SwiGLU, down + residual)."""
+    t = h.shape[0]
+    x = w8.w8i_rmsnorm(h, EPS)
+    qkv = w8.w8_linear_invariant_packed(*P["qkv"], x, t, T_PAD, P["n"]["qkv"])
+    h1 = w8.w8_linear_add_invariant_packed(*P["o"], qkv[:, :Q], h, t, T_PAD, P["n"]["o"])
+    x2 = w8.w8i_rmsnorm(h1, EPS)
+    a = w8.w8_linear_swiglu_invariant_packed(*P["gate_up"], x2, t, T_PAD, P["n"]["gate_up"] // 2)
+    return w8.w8_linear_add_invariant_packed(*P["down"], a, h1, t, T_PAD, P["n"]["down"])
+
+
+def test_fast_path_chain_gives_the_plain_bits():
+    """Thirty steps of random compositions through both paths: every lane state is bitwise the
+    same (packed = plain layout and fused = unfused composition, step after step)."""
+    say("case chain fast path: drawing the layer (seed 4)")
+    c = synth.chain_layer()
+    Wh = c["weights"]
+    W = {name: (i8(q), f16(s)) for name, (q, s) in Wh.items()}
+    P = {name: w8.w8_pack(*W[name]) for name in W}
+    P["n"] = {name: Wh[name][0].shape[0] for name in Wh}
+    plain = bf16(c["lanes"]).clone()
+    fast = plain.clone()
+    for i, lanes in enumerate(c["steps"][:30]):
+        idx = torch.as_tensor(lanes, dtype=torch.int64, device=plain.device)
+        a = layer(plain.index_select(0, idx).contiguous(), W)
+        b = fast_layer(fast.index_select(0, idx).contiguous(), P)
+        plain.index_copy_(0, idx, a)
+        fast.index_copy_(0, idx, b)
+        assert np.array_equal(bits(a), bits(b)), f"step {i} (t={len(lanes)}): fast path differs"
+    say("case chain fast path: 30 steps bitwise identical")
