@@ -29,7 +29,8 @@
 //  * The fp16 group scale is applied to that fp32 group sum in fp64 (the
 //    product is exact there); the fp64 result is rounded once to bf16.
 //  * Every one of the T_pad columns goes through the matrix core for every t;
-//    columns >= t read column t - 1 (valid memory) and are never stored.
+//    columns >= t load as zeros without a memory access (an offset past the
+//    activation buffer's range) and are never stored.
 //  * No atomics; nothing depends on t, T_pad, N or the device.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -118,6 +119,12 @@ __host__ __device__ constexpr int split_lds_scale_bytes(int NT, int D) {
 __device__ __forceinline__ uint32_t xs_off(int a, int p) { return (uint32_t)(a * 128 + 16 * (p ^ ((a >> 1) & 7))); }
 __device__ __forceinline__ uint32_t xs_piece(int a, int lane) { return (uint32_t)((lane & 7) ^ ((a >> 1) & 7)); }
 
+// Byte offset given to the activation loads of padding columns (j >= t): past
+// the end of any activation buffer (t <= 64 rows of at most 2^24 bf16 is at
+// most 2^31 bytes), so the buffer descriptor's range check returns zeros and
+// no memory is read; the stage and piece offsets added to it stay below 2^32.
+constexpr uint32_t kPadColumnOffset = 0x80000000u;
+
 // s_waitcnt that waits until at most N vector-memory operations are pending
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -175,8 +182,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int g_begin = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave));
     const int g_end = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave + 1));
 
-    // Rows past N read row N-1 and columns past t read column t-1 (valid
-    // memory, results never stored); the descriptors' ranges bound every access.
+    // Rows past N read row N-1 (valid memory, results never stored); padding
+    // columns (j >= t) load as zeros without a memory access (kPadColumnOffset);
+    // the descriptors' ranges bound every access.
     // packed layout: whole strips of P = ceil(G/2) stage blocks (2 KB of codes, 128 bytes of scales)
     const int64_t P = (G + 1) / 2;
     const int64_t strips = (N + kRows - 1) / kRows;
@@ -228,8 +236,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
         const int a = 8 * i + (lane >> 3);
-        const int jc = a < t ? a : t - 1;
-        xd_off[i] = (uint32_t)(jc * ldx) * 2u + 16u * xs_piece(a, lane);
+        xd_off[i] = (a < t ? (uint32_t)(a * ldx) * 2u : kPadColumnOffset) + 16u * xs_piece(a, lane);
     }
     const int r = lane & 31;  // weight row of this lane after the swaps (B column, D column)
     const int c = lane >> 5;
@@ -507,8 +514,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         const int m = kXLoads * wave + i;
         const int st = m / (4 * NT), tt = (m / 4) % NT;
         const int a = 32 * tt + 8 * (m % 4) + (lane >> 3);
-        const int jc = a < t ? a : t - 1;
-        xg_off[i] = (uint32_t)(jc * ldx) * 2u + (uint32_t)st * 64u * 2u + 16u * xs_piece(a, lane);
+        xg_off[i] = (a < t ? (uint32_t)(a * ldx) * 2u : kPadColumnOffset) + (uint32_t)st * 64u * 2u +
+                    16u * xs_piece(a, lane);
         xl_off[i] = (uint32_t)(st * kStageBytes + tt * kXTileBytes + (8 * (m % 4)) * 128);
     }
 
