@@ -11,19 +11,24 @@
 // Design for gfx950 (CDNA4):
 //  * The K plan is a function of K alone: 8 contiguous K-slices made of whole
 //    pairs of 32-element groups, the first four twice as long as the last
-//    four (kslice_begin), each summed in ascending
-//    group order in fp64, the 8 slice sums combined by a left fold.  Two
-//    kernels run this same plan and give the same bits for every row:
+//    four (kslice_begin); each slice is summed in ascending group order in
+//    fp64 and the 8 slice sums are combined by a left fold.  Two kernels run
+//    this same plan and give the same bits for every row:
 //    - gemm_w8g32_split_lds: one workgroup = 32 output rows x all K, its 8
-//      waves take the 8 slices; activations and scales are staged in LDS by
-//      direct loads; the slice sums meet in LDS and are folded there.
+//      waves take the 8 slices; activations (and, for the plain layout, the
+//      scales) are staged in LDS by direct loads; each wave parks its slice
+//      sum in LDS, one barrier, and the waves fold and store.  Template
+//      options: the store epilogue (plain, + residual, SwiGLU of gate/up row
+//      pairs) and the weight layout (plain row-major or packed).
 //    - gemm_w8g32_tiles (large N, T_pad <= 32): persistent workgroups stream
 //      256-row tiles; each wave owns a 32-row strip and walks all of K,
 //      keeping the running slice sum and the fold in registers, while the
 //      activation stage is shared through a double-buffered LDS ring.
-//  * Loads are coalesced: one instruction covers 16 rows x 64 contiguous
-//    bytes (two groups); v_permlane16_swap restores the matrix-core layout.
-//    Each group's 32 products per output are summed by two chained
+//  * Weight loads are coalesced.  Plain layout: one instruction covers 16 rows
+//    x 64 contiguous bytes (two groups) and v_permlane16_swap restores the
+//    matrix-core layout.  Packed layout (w8inv_pack.hip): one instruction
+//    reads 1 KB of whole cache lines already in the matrix-core lane order.
+//  * Each group's 32 products per output are summed by two chained
 //    v_mfma_f32_32x32x16_bf16 (A = activations, B = weights) into fp32 from
 //    zero; int8 -> bf16 is exact (7 significant bits).
 //  * The fp16 group scale is applied to that fp32 group sum in fp64 (the
@@ -85,15 +90,16 @@ __device__ __forceinline__ void swap16(u32x4& a, u32x4& b) {
 
 // ----------------------------------------------------------------------------
 // Split-K: one workgroup = 32 output rows x all K, its 8 waves take the 8
-// K-slices, the slice sums meet in LDS.  Activations and scales are staged in
-// LDS by direct loads (buffer_load ... lds).  Every wave re-reads its slice's
+// K-slices, the slice sums meet in LDS.  Activations are staged in LDS by
+// direct loads (buffer_load ... lds).  Every wave re-reads its slice's
 // activations from L2, and what that costs is the number of cache lines
 // touched, not the bytes: each direct load covers 8 columns x 128 bytes (whole
 // lines) and lands in a per-wave LDS ring of depth D, from which the
-// matrix-core operands are read.  The strip's scales (rows n0 .. n0+31) are
-// one contiguous block of 64 G bytes and are copied to LDS before the main
-// loop when they fit beside the ring; otherwise each stage loads its scales
-// with the weights.
+// matrix-core operands are read.  Plain layout: the strip's scales (rows
+// n0 .. n0+31) are one contiguous block of 64 G bytes and are copied to LDS
+// before the main loop when they fit beside the ring; otherwise each stage
+// loads its scales with the weights.  Packed layout: each stage loads its
+// scales as one 128-byte line.
 // ----------------------------------------------------------------------------
 #define W8I_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
