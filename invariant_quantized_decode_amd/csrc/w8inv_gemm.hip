@@ -27,7 +27,8 @@
 //  * Weight loads are coalesced.  Plain layout: one instruction covers 16 rows
 //    x 64 contiguous bytes (two groups) and v_permlane16_swap restores the
 //    matrix-core layout.  Packed layout (w8inv_pack.hip): one instruction
-//    reads 1 KB of whole cache lines already in the matrix-core lane order.
+//    reads 1 KB of whole cache lines already in the matrix-core lane order,
+//    with the nontemporal cache policy (each byte is read once).
 //  * Each group's 32 products per output are summed by two chained
 //    v_mfma_f32_32x32x16_bf16 (A = activations, B = weights) into fp32 from
 //    zero; int8 -> bf16 is exact (7 significant bits).
@@ -105,6 +106,13 @@ __device__ __forceinline__ void swap16(u32x4& a, u32x4& b) {
 
 constexpr int kXTileBytes = 32 * 128;  // 32 columns x one stage of bf16
 constexpr int kLdsDmaBytes = 1024;     // bytes of one wave-wide 16-byte direct load
+
+// Cache policy of the packed layout's weight and scale loads: nontemporal.
+// Every packed byte is read once, by one load of whole lines, so nothing is
+// gained by keeping it in L2 (measured 2-7% faster across the decode shapes).
+// The plain layout keeps the default policy: each of its weight loads covers
+// half of a 128-byte line whose other half the next stage reads, from L2.
+constexpr int kStreamOnce = 2;  // the nt bit of the buffer load's cache-policy operand
 
 // one ring slot (the stage of all 8 waves) for NT 32-column tiles
 __host__ __device__ constexpr int split_lds_slot_bytes(int NT) { return kKSlices * NT * kXTileBytes; }
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
         if constexpr (PK) {
             const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
-            sp = __builtin_amdgcn_raw_buffer_load_b32(sr, pk_s, g * 64, 0);
+            sp = __builtin_amdgcn_raw_buffer_load_b32(sr, pk_s, g * 64, kStreamOnce);
         } else if constexpr (!LS) {
             const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
             sc[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * g, 0, 0);
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             w[i] = __builtin_bit_cast(
-                u32x4, PK ? __builtin_amdgcn_raw_buffer_load_b128(wr, pk_w + 1024u * i, g * 1024, 0)
+                u32x4, PK ? __builtin_amdgcn_raw_buffer_load_b128(wr, pk_w + 1024u * i, g * 1024, kStreamOnce)
                           : __builtin_amdgcn_raw_buffer_load_b128(wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i)
@@ -555,9 +563,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             const uint32_t blk = (uint32_t)(strip * P + g / 2);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                st.w[i] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, blk * 2048u + 1024u * i + 16u * lane, 0, 0));
-            st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, blk * 128u + 4u * r, 0, 0);
+                st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        wr, blk * 2048u + 1024u * i + 16u * lane, 0, kStreamOnce));
+            st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, blk * 128u + 4u * r, 0, kStreamOnce);
             return;
         }
 #pragma unroll
