@@ -35,9 +35,13 @@
 //  * The fp16 group scale is applied to that fp32 group sum in fp64 (the
 //    product is exact there); the fp64 result is rounded once to bf16.
 //  * Every one of the T_pad columns goes through the matrix core for every t;
-//    columns >= t load as zeros without a memory access (an offset past the
-//    activation buffer's range) and are never stored.
-//  * No atomics; nothing depends on t, T_pad, N or the device.
+//    columns >= t are zeros and are never stored.  A padding column inside a
+//    direct load's 8 columns loads as zeros without a memory access (an
+//    offset past the activation buffer's range); a load whose 8 columns are
+//    all padding is not issued at all, its LDS region zeroed once (the one
+//    thing t selects: how many activation loads a stage issues).
+//  * No atomics; the arithmetic of a column -- K plan, MFMA sequence,
+//    roundings -- depends on neither t, its neighbours, N nor the device.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -164,8 +168,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     constexpr int kSlotBytes = split_lds_slot_bytes(NT);
     constexpr int kScaleBytes = LS ? split_lds_scale_bytes(NT, D) : 16;
     constexpr int kXLoads = 4 * NT;                   // direct loads of 8 columns x 128 bytes per stage
-    // weights + activations (+ scales)
-    constexpr int kLoadsPerStage = 2 + kXLoads + (PK ? 1 : LS ? 0 : 2);
     static_assert(!PK || !LS, "packed layout: scales come with each stage");
     static_assert(kScaleBytes > 0, "LDS");
     // one array per ring slot, so the compiler can wait for each slot's loads alone
@@ -293,7 +295,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     // stage starting at group g; `single` loads group g alone in position 0
     // (the odd last group)
     // (packed: the stage block of group g, both groups, and its scale line)
-    auto load_stage = [&](int g, u32x4 (&w)[2], uint16_t (&sc)[2], uint32_t& sp, unsigned char* xs, bool single) {
+    // (XLc: the number of direct activation loads issued, see `run` below)
+    auto load_stage = [&](auto XLc, int g, u32x4 (&w)[2], uint16_t (&sc)[2], uint32_t& sp, unsigned char* xs,
+                          bool single) {
+        constexpr int XL = decltype(XLc)::value;
         const bool live = single || g <= last_full;
         const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
         const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
                 u32x4, PK ? __builtin_amdgcn_raw_buffer_load_b128(wr, pk_w + 1024u * i, g * 1024, kStreamOnce)
                           : __builtin_amdgcn_raw_buffer_load_b128(wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
 #pragma unroll
-        for (int i = 0; i < kXLoads; ++i)
+        for (int i = 0; i < XL; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, W8I_LDS(xs + wave * kStageBytes + i * kLdsDmaBytes), 16,
                                                      xd_off[i], g * (2 * kGroup), 0, 0);
     };
@@ -335,79 +340,117 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         }
     };
 
-    u32x4 ring[D][2];
-    uint16_t sring[D][2];
-    uint32_t pring[D];
-    if (full > 0) {
+    // The stages' loads, for XL = XLc direct activation loads per stage.  A
+    // direct load covers 8 columns; those whose 8 columns are all padding
+    // (j >= t) are not issued, and their LDS regions are zeroed once here, so
+    // the matrix core sees the same zeros for padding columns as it would
+    // from loads (and, as for every padding column, nothing of them is
+    // stored).  What is computed for the live columns -- the K plan, every
+    // MFMA and every rounding -- does not depend on XL; the choice only
+    // spares the memory pipeline 1 KB per skipped load (at t = 1, three of
+    // every four activation loads).
+    auto run = [&](auto XLc) {
+        constexpr int XL = decltype(XLc)::value;
+        constexpr int kLPS = 2 + XL + (PK ? 1 : LS ? 0 : 2);  // loads per stage
+        if constexpr (XL < kXLoads) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) load_stage(g_begin + 2 * u, ring[u], sring[u], pring[u], slot(u), false);
-    }
-    if constexpr (LS) {
-        if (full > 0)
-            wait_vm<kLoadsPerStage * D>();  // this wave's scale loads have landed
-        else
-            wait_vm<0>();
-        // Every wave's scale loads have landed.  A plain barrier: __syncthreads()
-        // would also wait for the activation ring's loads (its release fence
-        // covers all pending LDS writes).  The signal fences keep the compiler
-        // from moving LDS accesses across it.
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    }
+            for (int u = 0; u < D; ++u)
+#pragma unroll
+                for (int i = XL; i < kXLoads; ++i)
+                    *reinterpret_cast<u32x4*>(slot(u) + wave * kStageBytes + i * kLdsDmaBytes + 16 * lane) =
+                        u32x4{0u, 0u, 0u, 0u};
+        }
+        u32x4 ring[D][2];
+        uint16_t sring[D][2];
+        uint32_t pring[D];
+        if (full > 0) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) load_stage(XLc, g_begin + 2 * u, ring[u], sring[u], pring[u], slot(u), false);
+        }
+        if constexpr (LS) {
+            if (full > 0)
+                wait_vm<kLPS * D>();  // this wave's scale loads have landed
+            else
+                wait_vm<0>();
+            // Every wave's scale loads have landed.  A plain barrier: __syncthreads()
+            // would also wait for the activation ring's loads (its release fence
+            // covers all pending LDS writes).  The signal fences keep the compiler
+            // from moving LDS accesses across it.
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
 
-    int g = g_begin;
-    if (full > 0) {
-        const int nblocks = full / D;
-        // Stage q's loads are complete once only the D - 1 later stages'
-        // loads are pending.  The wait is explicit: the compiler's own
-        // tracking of direct-to-LDS loads is not relied on.
-        for (int blk = 0; blk < nblocks; ++blk) {
+        int g = g_begin;
+        if (full > 0) {
+            const int nblocks = full / D;
+            // Stage q's loads are complete once only the D - 1 later stages'
+            // loads are pending.  The wait is explicit: the compiler's own
+            // tracking of direct-to-LDS loads is not relied on.
+            for (int blk = 0; blk < nblocks; ++blk) {
 #pragma unroll
-            for (int u = 0; u < D; ++u) {
-                wait_vm<kLoadsPerStage * (D - 1)>();
-                if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
-                step(ring[u], sring[u], pring[u], slot(u), 0, g);
-                step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                load_stage(g + 2 * D, ring[u], sring[u], pring[u], slot(u), false);
-                __builtin_amdgcn_sched_barrier(0);
-                g += 2;
+                for (int u = 0; u < D; ++u) {
+                    wait_vm<kLPS * (D - 1)>();
+                    if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
+                    step(ring[u], sring[u], pring[u], slot(u), 0, g);
+                    step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_stage(XLc, g + 2 * D, ring[u], sring[u], pring[u], slot(u), false);
+                    __builtin_amdgcn_sched_barrier(0);
+                    g += 2;
+                }
+            }
+            // the remaining full stages (fewer than D) were loaded already; after
+            // the u-th of them only D - 1 - u stages' loads are pending
+            auto tail_stage = [&](auto U) {
+                constexpr int u = decltype(U)::value;
+                if constexpr (u <= D - 2) {  // a tail has at most D - 1 stages
+                    wait_vm<kLPS * (D - 1 - u)>();
+                    if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
+                    step(ring[u], sring[u], pring[u], slot(u), 0, g);
+                    step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
+                    g += 2;
+                }
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            switch (full - nblocks * D) {
+                case 1: tail_stage(I0{}); break;
+                case 2: tail_stage(I0{}); tail_stage(I1{}); break;
+                case 3: tail_stage(I0{}); tail_stage(I1{}); tail_stage(I2{}); break;
+                default: break;
             }
         }
-        // the remaining full stages (fewer than D) were loaded already; after
-        // the u-th of them only D - 1 - u stages' loads are pending
-        auto tail_stage = [&](auto U) {
-            constexpr int u = decltype(U)::value;
-            if constexpr (u <= D - 2) {  // a tail has at most D - 1 stages
-                wait_vm<kLoadsPerStage * (D - 1 - u)>();
-                if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
-                step(ring[u], sring[u], pring[u], slot(u), 0, g);
-                step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
-                g += 2;
-            }
-        };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        switch (full - nblocks * D) {
-            case 1: tail_stage(I0{}); break;
-            case 2: tail_stage(I0{}); tail_stage(I1{}); break;
-            case 3: tail_stage(I0{}); tail_stage(I1{}); tail_stage(I2{}); break;
-            default: break;
+        if (odd) {
+            // the row's last group (slice 7 when K/32 is odd); the ring is drained
+            // and slot 0's region of this wave is free
+            // (packed: the block of the last pair, whose second group is padding)
+            u32x4 w1[2];
+            uint16_t s1[2];
+            uint32_t p1;
+            load_stage(XLc, g_end - 1, w1, s1, p1, xr0, true);
+            wait_vm<0>();
+            if constexpr (!PK) swap16(w1[0], w1[1]);
+            step(w1, s1, p1, xr0, 0, g_end - 1);
         }
-    }
-    if (odd) {
-        // the row's last group (slice 7 when K/32 is odd); the ring is drained
-        // and slot 0's region of this wave is free
-        // (packed: the block of the last pair, whose second group is padding)
-        u32x4 w1[2];
-        uint16_t s1[2];
-        uint32_t p1;
-        load_stage(g_end - 1, w1, s1, p1, xr0, true);
-        wait_vm<0>();
-        if constexpr (!PK) swap16(w1[0], w1[1]);
-        step(w1, s1, p1, xr0, 0, g_end - 1);
+    };
+    // one uniform branch per launch: XL = the column groups holding a live
+    // column, rounded up to 1, 2, 4 or all
+    {
+        const int live_groups = (t + 7) / 8;
+        if (live_groups <= 1) {
+            run(std::integral_constant<int, 1>{});
+        } else if (live_groups <= 2) {
+            run(std::integral_constant<int, 2>{});
+        } else if constexpr (kXLoads == 8) {
+            if (live_groups <= 4)
+                run(std::integral_constant<int, 4>{});
+            else
+                run(std::integral_constant<int, 8>{});
+        } else {
+            run(std::integral_constant<int, kXLoads>{});
+        }
     }
 
     // Left fold of the 8 slice sums, ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7,
@@ -495,7 +538,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     static_assert(kXLoads * kTileStrips * kLdsDmaBytes == kBlockBytes && kXLoads <= 4,
                   "a block's activations split evenly, at most 4 direct loads per wave");
     constexpr int LW = SC ? 2 : PK ? 3 : 4;                       // loads per stage (weights [+ scales])
-    constexpr int LX = kXLoads;                                   // activation loads per block
     constexpr int LS = SC ? 1 : 0;                                // scale-chunk loads per block
     // one array per buffer, so each buffer's direct loads are told apart
     __shared__ __align__(16) unsigned char xb0[kBlockBytes];
@@ -593,12 +635,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         const uint32_t off = (uint32_t)(row * G + block_g(b < nb ? b : nb - 1)) * 2u;
         return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? s_rsrc : s_none, off, 0, 0));
     };
-    // this wave's share of block b's activations, into buffer xb
-    auto load_x = [&](int b, unsigned char* xb) {
+    // this wave's share of block b's activations, into buffer xb (its first
+    // XL = XLc direct loads)
+    auto load_x = [&](auto XLc, int b, unsigned char* xb) {
+        constexpr int XL = decltype(XLc)::value;
         const bool live = b < nb;
         const uint32_t g_off = (uint32_t)block_g(live ? b : nb - 1) * 64u;
 #pragma unroll
-        for (int i = 0; i < kXLoads; ++i)
+        for (int i = 0; i < XL; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? x_rsrc : x_none, W8I_LDS(xb + xl_off[i]), 16,
                                                      xg_off[i] + g_off, 0, 0, 0);
     };
@@ -624,103 +668,134 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         ++slice;
     };
 
-    WStage ring[kBlockStages];
-    u32x4 sc0 = {}, sc1 = {};
-    // prologue: block 0's activations, scales and weights, in this order (the
-    // wait counts below depend on it; the scheduling barriers keep it)
-    load_x(0, xb0);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SC) sc0 = load_scales(0);
-    __builtin_amdgcn_sched_barrier(0);
+    // The loop, for XL = XLc direct activation loads per wave per block.  With
+    // the packed layout, wave w's loads are the 4 column groups of stage w of
+    // the block, so every wave has the same XL live ones; loads whose 8
+    // columns are all padding are not issued and their LDS regions are
+    // zeroed once at entry (the same zeros the loads would bring; what is
+    // computed for live columns does not depend on XL).  The plain layout's
+    // 4-stage blocks give a stage's column groups to two waves, so it always
+    // loads them all.
+    auto run = [&](auto XLc) {
+        constexpr int XL = decltype(XLc)::value;
+        if constexpr (XL < kXLoads) {
 #pragma unroll
-    for (int u = 0; u < kBlockStages; ++u) {
-        load_stage(0, u, ring[u]);
+            for (int i = XL; i < kXLoads; ++i) {
+                *reinterpret_cast<u32x4*>(xb0 + xl_off[i] + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(xb1 + xl_off[i] + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();  // (no loads are in flight yet)
+        }
+        WStage ring[kBlockStages];
+        u32x4 sc0 = {}, sc1 = {};
+        // prologue: block 0's activations, scales and weights, in this order (the
+        // wait counts below depend on it; the scheduling barriers keep it)
+        load_x(XLc, 0, xb0);
         __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // block b: activations in xs, scales in sc; block b + 1 is loaded into
-    // xn and sn.  Blocks go in pairs so that buffers and scale registers are
-    // named statically; a phantom block pads an odd count.
-    auto block = [&](int b, const unsigned char* xs, unsigned char* xn, const u32x4& sc, u32x4& sn) {
-        // this wave's direct loads of block b have landed once only the loads
-        // issued after them are pending; the barrier publishes all waves'
-        wait_vm<LS + kBlockStages * LW>();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // every wave is past block b - 1, so its buffer takes block b + 1
+        if constexpr (SC) sc0 = load_scales(0);
         __builtin_amdgcn_sched_barrier(0);
-        load_x(b + 1, xn);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (SC) sn = load_scales(b + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        const bool live = b < nb;
-        const int g0 = block_g(b);
 #pragma unroll
         for (int u = 0; u < kBlockStages; ++u) {
-            // stage u's loads have landed once only the loads issued after
-            // them are pending (the same count for every stage)
-            wait_vm<(kBlockStages - 1) * LW + LX + LS>();
-            WStage& cur = ring[u];
-            const int g = g0 + 2 * u;
-            if (live && g < G) {
-                if constexpr (!PK) swap16(cur.w[0], cur.w[1]);
-                while (kslice_begin(G, slice + 1) <= g) fold_slice();
-                const int ng = (g + 1 < G) ? 2 : 1;
+            load_stage(0, u, ring[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // block b: activations in xs, scales in sc; block b + 1 is loaded into
+        // xn and sn.  Blocks go in pairs so that buffers and scale registers are
+        // named statically; a phantom block pads an odd count.
+        auto block = [&](int b, const unsigned char* xs, unsigned char* xn, const u32x4& sc, u32x4& sn) {
+            // this wave's direct loads of block b have landed once only the loads
+            // issued after them are pending; the barrier publishes all waves'
+            wait_vm<LS + kBlockStages * LW>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            // every wave is past block b - 1, so its buffer takes block b + 1
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(XLc, b + 1, xn);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (SC) sn = load_scales(b + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool live = b < nb;
+            const int g0 = block_g(b);
 #pragma unroll
-                for (int gs = 0; gs < 2; ++gs) {
-                    if (gs >= ng) break;  // odd G: the tile's last stage has one group
-                    const bf16x8 b_lo = dequant8(cur.w[gs].x, cur.w[gs].y);
-                    const bf16x8 b_hi = dequant8(cur.w[gs].z, cur.w[gs].w);
-                    uint16_t s16;
-                    if constexpr (SC)
-                        s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
-                    else if constexpr (PK)
-                        s16 = (uint16_t)(cur.sp >> (16 * gs));
-                    else
-                        s16 = cur.s[gs];
-                    const double scale = (double)(float)__builtin_bit_cast(_Float16, s16);
+            for (int u = 0; u < kBlockStages; ++u) {
+                // stage u's loads have landed once only the loads issued after
+                // them are pending (the same count for every stage)
+                wait_vm<(kBlockStages - 1) * LW + XL + LS>();
+                WStage& cur = ring[u];
+                const int g = g0 + 2 * u;
+                if (live && g < G) {
+                    if constexpr (!PK) swap16(cur.w[0], cur.w[1]);
+                    while (kslice_begin(G, slice + 1) <= g) fold_slice();
+                    const int ng = (g + 1 < G) ? 2 : 1;
 #pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) {
-                        const unsigned char* xt = xs + u * kStageBytes + tt * kXTileBytes;
-                        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c));
-                        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c + 1));
-                        const f32x16 zero = {};
-                        f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo,
-                                                                           zero, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
-                        const int nv = (tt == NT - 1) ? kLastValues : 16;
+                    for (int gs = 0; gs < 2; ++gs) {
+                        if (gs >= ng) break;  // odd G: the tile's last stage has one group
+                        const bf16x8 b_lo = dequant8(cur.w[gs].x, cur.w[gs].y);
+                        const bf16x8 b_hi = dequant8(cur.w[gs].z, cur.w[gs].w);
+                        uint16_t s16;
+                        if constexpr (SC)
+                            s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
+                        else if constexpr (PK)
+                            s16 = (uint16_t)(cur.sp >> (16 * gs));
+                        else
+                            s16 = cur.s[gs];
+                        const double scale = (double)(float)__builtin_bit_cast(_Float16, s16);
 #pragma unroll
-                        for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(scale, (double)d[v], acc[tt][v]);
+                        for (int tt = 0; tt < NT; ++tt) {
+                            const unsigned char* xt = xs + u * kStageBytes + tt * kXTileBytes;
+                            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c));
+                            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c + 1));
+                            const f32x16 zero = {};
+                            f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo,
+                                                                               zero, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0,
+                                                                        0);
+                            const int nv = (tt == NT - 1) ? kLastValues : 16;
+#pragma unroll
+                            for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(scale, (double)d[v], acc[tt][v]);
+                        }
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                load_stage(b + 1, u, cur);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            load_stage(b + 1, u, cur);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (live && b % nbt == nbt - 1) {
-            // the tile's last block: fold the remaining slices, store this strip
-            while (slice < kKSlices) fold_slice();
-            const int64_t n = strip_row(b) + r;
-            if (n < N) {
+            if (live && b % nbt == nbt - 1) {
+                // the tile's last block: fold the remaining slices, store this strip
+                while (slice < kKSlices) fold_slice();
+                const int64_t n = strip_row(b) + r;
+                if (n < N) {
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
+                    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                    for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
-                        const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
-                        if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(total[tt][v]);
-                    }
+                        for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
+                            const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
+                            if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(total[tt][v]);
+                        }
+                }
+                slice = 0;
             }
-            slice = 0;
+        };
+        for (int b = 0; b < nb; b += 2) {
+            block(b, xb0, xb1, sc0, sc1);
+            block(b + 1, xb1, xb0, sc1, sc0);
         }
+        // the phantom block's loads are still in flight: drain them before exit
+        wait_vm<0>();
     };
-    for (int b = 0; b < nb; b += 2) {
-        block(b, xb0, xb1, sc0, sc1);
-        block(b + 1, xb1, xb0, sc1, sc0);
+    if constexpr (PK) {
+        const int live_groups = (t + 7) / 8;
+        if (live_groups <= 1)
+            run(std::integral_constant<int, 1>{});
+        else if (live_groups <= 2)
+            run(std::integral_constant<int, 2>{});
+        else
+            run(std::integral_constant<int, kXLoads>{});
+    } else {
+        run(std::integral_constant<int, kXLoads>{});
     }
-    // the phantom block's loads are still in flight: drain them before exit
-    wait_vm<0>();
 }
 
 // Tiles of the persistent kernel; it is used when there are enough of them
