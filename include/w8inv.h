@@ -78,9 +78,9 @@ const char *w8i_version(void);
  *     summed by bf16 matrix-core instructions into fp32 starting from zero;
  *   - that group sum is multiplied by its fp16 scale and accumulated in fp64;
  *   - K is cut into 8 contiguous slices of whole pairs of groups, slices
- *     0..3 twice as long as slices 4..7: with G = K/32 groups, P = floor(G/2)
- *     pairs and c = (0, 2, 4, 6, 8, 9, 10, 11, 12), slice i covers groups
- *     [2*floor(P*c_i/12), 2*floor(P*c_{i+1}/12)) and, when G is odd, slice 7
+ *     0..3 three times as long as slices 4..7: with G = K/32 groups, P =
+ *     floor(G/2) pairs and c = (0, 3, 6, 9, 12, 13, 14, 15, 16), slice i covers
+ *     groups [2*floor(P*c_i/16), 2*floor(P*c_{i+1}/16)) and, when G is odd, slice 7
  *     also takes the last group.  Each slice is summed in ascending group order
  *     (an empty slice is +0) and the 8 slice sums are combined by the left
  *     fold ((((((s0+s1)+s2)+s3)+s4)+s5)+s6)+s7.  The plan depends on K only;

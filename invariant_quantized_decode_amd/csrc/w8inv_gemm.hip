@@ -10,8 +10,8 @@
 //
 // Design for gfx950 (CDNA4):
 //  * The K plan is a function of K alone: 8 contiguous K-slices made of whole
-//    pairs of 32-element groups, the first four twice as long as the last
-//    four (kslice_begin); each slice is summed in ascending group order in
+//    pairs of 32-element groups, the first four three times as long as the
+//    last four (kslice_begin); each slice is summed in ascending group order in
 //    fp64 and the 8 slice sums are combined by a left fold.  Two kernels run
 //    this same plan and give the same bits for every row:
 //    - gemm_w8g32_split_lds: one workgroup = 32 output rows x all K, its 8

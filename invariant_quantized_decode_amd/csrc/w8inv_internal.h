@@ -13,18 +13,18 @@ constexpr int kGroup = 32;   // K elements per fp16 scale (W8G32)
 constexpr int kKSlices = 8;  // fixed number of K-slices per output, for every shape
 
 // First group of K-slice i when K holds G groups.  Slices are made of whole
-// pairs of groups, slices 0..3 twice as long as slices 4..7: with P = G/2
-// pairs and cumulative weights c_i = 0, 2, 4, 6, 8, 9, 10, 11, 12, slice i
-// covers pairs [floor(P*c_i/12), floor(P*c_{i+1}/12)), and when G is odd the
-// row's last group closes slice 7.  The whole K-reduction plan is this
-// function of K alone.  (Why unequal: the split kernel gives slice i to wave
-// i, and waves 0..3 -- the older wave on each SIMD -- stream their loads
-// ahead of waves 4..7; with equal slices the younger waves finished ~2.5 us
-// later, alone on their SIMDs.)
+// pairs of groups, slices 0..3 three times as long as slices 4..7: with P =
+// G/2 pairs and cumulative weights c_i = 0, 3, 6, 9, 12, 13, 14, 15, 16,
+// slice i covers pairs [floor(P*c_i/16), floor(P*c_{i+1}/16)), and when G is
+// odd the row's last group closes slice 7.  The whole K-reduction plan is
+// this function of K alone.  (Why unequal: the split kernel gives slice i to
+// wave i, and waves 0..3 -- the older wave on each SIMD -- stream their loads
+// ahead of waves 4..7, whose first loads queue behind theirs; with equal
+// slices the younger waves finished ~2.5 us later, alone on their SIMDs.)
 __host__ __device__ __forceinline__ int64_t kslice_begin(int64_t G, int i) {
     if (i >= kKSlices) return G;
-    const int64_t c = i <= 4 ? 2 * i : 4 + i;
-    return 2 * (((G / 2) * c) / 12);
+    const int64_t c = i <= 4 ? 3 * i : 8 + i;
+    return 2 * (((G / 2) * c) / 16);
 }
 
 // What the projection kernel stores for output (j, n).
