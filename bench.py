@@ -187,6 +187,11 @@ def main():
         torch.cuda.synchronize()
     copy_gbs = 5 * 2 * a.numel() / (c0.elapsed_time(c1) / 1e3) / 1e9
     del a, b
+    # context: the practical read ceiling of one launch over the same bytes, and the dense bf16
+    # matrix-core rate (calibration kernels of libw8calib.so)
+    from invariant_quantized_decode_amd import calib
+    read_gbs = calib.stream_read_gbs(wbytes)
+    mfma_tflops = calib.mfma_bf16_tflops()
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
@@ -250,6 +255,14 @@ def main():
                                    "hbm_frac": r(alt_one["weight_gbs"] / HBM_PEAK_GBS, 4)}},
         "t_invariance": inv_ok,
         "device_copy_gbs": r(copy_gbs, 1),
+        "context": {
+            "stream_read_gbs": {str(k): r(v, 1) for k, v in read_gbs.items()},
+            "stream_read_note": f"bare nontemporal read of the {wbytes} weight+scale bytes in one launch, by "
+                                "workgroup count (the projection uses " + str((N + 31) // 32) + ")",
+            "value_vs_best_read": r(full["weight_gbs"] / max(read_gbs.values()), 3),
+            "t1_vs_best_read": r(one["weight_gbs"] / max(read_gbs.values()), 3),
+            "mfma_bf16_tflops_measured": r(mfma_tflops, 1),
+        },
         "roofline": roof,
         "cpu_baseline": cpu,
     }

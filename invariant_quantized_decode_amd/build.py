@@ -12,6 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw8inv.so")
+# calibration kernels (include/w8calib.h): a separate library, outside the decode path
+CALIB_LIB = os.path.join(PKG, "libw8calib.so")
+CALIB_SOURCES = ["w8calib.hip"]
 
 SOURCES = ["w8inv_api.hip", "w8inv_gemm.hip", "w8inv_logprob.hip", "w8inv_glue.hip", "w8inv_pack.hip",
            "w8inv_argmax.hip"]
@@ -39,17 +42,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc link failed")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(CALIB_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + CALIB_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     return LIB
 
 

@@ -201,3 +201,25 @@ def test_binding_refuses_host_tensors():
         w8.w8_linear_invariant(q, s, x, 4, 32, y=torch.zeros((4, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         w8.w8i_exp32(torch.zeros(8), y=torch.zeros(8))
+
+
+def test_calibration_library_exports_its_header_and_validates():
+    """libw8calib.so (the measurement helpers of include/w8calib.h, outside the decode path) exports
+    what its header declares and rejects bad arguments on the host."""
+    from invariant_quantized_decode_amd import calib
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "w8calib.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(w8c_[a-z0-9_]*)\s*\(", text)))
+    assert names == ["w8c_mfma_bf16", "w8c_stream_read"]
+    C = calib._lib()
+    for n in names:
+        assert hasattr(C, n), n
+    fake = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation first
+    assert C.w8c_stream_read(None, 1024, 1, fake, 2048, None) == -1
+    assert C.w8c_stream_read(fake, 1000, 1, fake, 2048, None) == -2       # not a multiple of 16
+    assert C.w8c_stream_read(fake, 1024, 0, fake, 2048, None) == -2       # no workgroups
+    assert C.w8c_stream_read(ctypes.c_void_p(264), 1024, 1, fake, 2048, None) == -3
+    assert C.w8c_stream_read(fake, 1024, 2, fake, 2048, None) == -6       # sink for one workgroup only
+    assert C.w8c_mfma_bf16(1, 1, None, 1024, None) == -1
+    assert C.w8c_mfma_bf16(1, 0, fake, 1024, None) == -2
+    assert C.w8c_mfma_bf16(0, 1, fake, 1024, None) == -2
+    assert C.w8c_mfma_bf16(2, 1, fake, 1024, None) == -6
