@@ -277,16 +277,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int len = g_end - g_begin;
     const int full = len >> 1;
     const int odd = len & 1;
-    const int last_full = g_begin + 2 * (full > 0 ? full - 1 : 0);
 
-    // Prefetches past the slice's last full stage keep the loop free of
-    // branches; they go through descriptors with an empty range, which return
-    // zeros without touching memory (the slot they fill is never read).
-    const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t x_none =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t s_none =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(S), (short)0, 0, 0x00020000);
     // this lane's row of scales (per-stage scale loads), and its place in LDS
     const uint32_t s_row_off = (uint32_t)(row_of(r) * G) * 2u;
     const int s_row_lds = EPI == kEpiSwiGLU ? (r >> 4) * (s_pieces * kLdsDmaBytes / 2) + (r & 15) * G : r * G;
@@ -299,25 +290,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     auto load_stage = [&](auto XLc, int g, u32x4 (&w)[2], uint16_t (&sc)[2], uint32_t& sp, unsigned char* xs,
                           bool single) {
         constexpr int XL = decltype(XLc)::value;
-        const bool live = single || g <= last_full;
-        const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
-        const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
         if constexpr (PK) {
-            const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
-            sp = __builtin_amdgcn_raw_buffer_load_b32(sr, pk_s, g * 64, kStreamOnce);
+            sp = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, pk_s, g * 64, kStreamOnce);
         } else if constexpr (!LS) {
-            const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
-            sc[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * g, 0, 0);
-            sc[1] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_row_off + 2u * (single ? g : g + 1), 0, 0);
+            sc[0] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_row_off + 2u * g, 0, 0);
+            sc[1] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_row_off + 2u * (single ? g : g + 1), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             w[i] = __builtin_bit_cast(
-                u32x4, PK ? __builtin_amdgcn_raw_buffer_load_b128(wr, pk_w + 1024u * i, g * 1024, kStreamOnce)
-                          : __builtin_amdgcn_raw_buffer_load_b128(wr, single ? w_off[i] : w_off_gs[i], g * kGroup, 0));
+                u32x4, PK ? __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, pk_w + 1024u * i, g * 1024, kStreamOnce)
+                          : __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, single ? w_off[i] : w_off_gs[i], g * kGroup,
+                                                                  0));
 #pragma unroll
         for (int i = 0; i < XL; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, W8I_LDS(xs + wave * kStageBytes + i * kLdsDmaBytes), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, W8I_LDS(xs + wave * kStageBytes + i * kLdsDmaBytes), 16,
                                                      xd_off[i], g * (2 * kGroup), 0, 0);
     };
     // group gs of the stage (weights already swapped), acc += s * D_g in fp64
@@ -363,63 +350,147 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         u32x4 ring[D][2];
         uint16_t sring[D][2];
         uint32_t pring[D];
-        if (full > 0) {
-#pragma unroll
-            for (int u = 0; u < D; ++u) load_stage(XLc, g_begin + 2 * u, ring[u], sring[u], pring[u], slot(u), false);
-        }
-        if constexpr (LS) {
-            if (full > 0)
-                wait_vm<kLPS * D>();  // this wave's scale loads have landed
-            else
-                wait_vm<0>();
-            // Every wave's scale loads have landed.  A plain barrier: __syncthreads()
-            // would also wait for the activation ring's loads (its release fence
-            // covers all pending LDS writes).  The signal fences keep the compiler
-            // from moving LDS accesses across it.
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        }
-
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using ID = std::integral_constant<int, D>;
+        // (LS) the strip's scales must be in LDS before the first stage: wait for
+        // this wave's scale loads (issued before the ring: only the `after`
+        // loads issued since may stay pending), then a plain barrier --
+        // __syncthreads() would also wait for the ring's loads (its release
+        // fence covers all pending LDS writes); the signal fences keep the
+        // compiler from moving LDS accesses across it.
+        auto scales_ready = [&](auto After) {
+            if constexpr (LS) {
+                wait_vm<decltype(After)::value>();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_s_barrier();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
+        };
         int g = g_begin;
-        if (full > 0) {
-            const int nblocks = full / D;
-            // Stage q's loads are complete once only the D - 1 later stages'
-            // loads are pending.  The wait is explicit: the compiler's own
-            // tracking of direct-to-LDS loads is not relied on.
-            for (int blk = 0; blk < nblocks; ++blk) {
-#pragma unroll
-                for (int u = 0; u < D; ++u) {
-                    wait_vm<kLPS * (D - 1)>();
-                    if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
-                    step(ring[u], sring[u], pring[u], slot(u), 0, g);
-                    step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_stage(XLc, g + 2 * D, ring[u], sring[u], pring[u], slot(u), false);
+        // the stage in ring slot u (its loads have landed)
+        auto compute = [&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
+            step(ring[u], sring[u], pring[u], slot(u), 0, g);
+            step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
+        };
+        // Only real stages are loaded: the first min(D, full) up front, then
+        // stage q + D right after stage q is computed, while q + D < full.
+        // Stage q's loads are complete once only the loads of the stages
+        // after it that have been issued are pending (D - 1 of them while
+        // the ring is full).  The waits are explicit: the compiler's own
+        // tracking of direct-to-LDS loads is not relied on.  Every stage body
+        // below is a separate, sequential copy (alternative copies of the same
+        // stages in switch cases made the compiler merge them and double the
+        // live registers).
+        auto wait_stages = [&](int pending) {  // s_waitcnt takes an immediate
+            switch (pending) {
+                case 0: wait_vm<0>(); break;
+                case 1: wait_vm<kLPS>(); break;
+                case 2: if constexpr (D > 2) wait_vm<kLPS * 2>(); break;
+                default: if constexpr (D > 3) wait_vm<kLPS * 3>(); break;
+            }
+        };
+        auto prefetching = [&](auto U) {
+            constexpr int u = decltype(U)::value;
+            wait_vm<kLPS * (D - 1)>();
+            compute(U);
+            __builtin_amdgcn_sched_barrier(0);
+            load_stage(XLc, g + 2 * D, ring[u], sring[u], pring[u], slot(u), false);
+            __builtin_amdgcn_sched_barrier(0);
+            g += 2;
+        };
+        // the last n stages, the first of them in slot s0
+        auto last_one = [&](auto S0, auto Nn, auto Ii) {
+            constexpr int n = decltype(Nn)::value, i = decltype(Ii)::value;
+            if constexpr (i < n) {
+                wait_vm<kLPS * (n - 1 - i)>();
+                compute(std::integral_constant<int, (decltype(S0)::value + i) % D>{});
+                __builtin_amdgcn_sched_barrier(0);
+                g += 2;
+            }
+        };
+        auto last = [&](auto S0, auto Nn) {
+            last_one(S0, Nn, I0{});
+            last_one(S0, Nn, I1{});
+            last_one(S0, Nn, I2{});
+            last_one(S0, Nn, I3{});
+        };
+        // the final full ring: D stages in slots 0..D-1, of which the first r
+        // still prefetch (stage u then has D - 1 stages pending after it, the
+        // others D - 1 - u + r)
+        auto final_one = [&](auto U, int r) {
+            constexpr int u = decltype(U)::value;
+            if constexpr (u < D) {
+                wait_stages(u < r ? D - 1 : D - 1 - u + r);
+                compute(U);
+                __builtin_amdgcn_sched_barrier(0);
+                if (u < r) load_stage(XLc, g + 2 * D, ring[u], sring[u], pring[u], slot(u), false);
+                __builtin_amdgcn_sched_barrier(0);
+                g += 2;
+            }
+        };
+        // then the r < D stages those prefetched, in slots 0..r-1
+        auto after_one = [&](auto U, int r) {
+            constexpr int u = decltype(U)::value;
+            if constexpr (u < D - 1) {
+                if (u < r) {
+                    wait_stages(r - 1 - u);
+                    compute(U);
                     __builtin_amdgcn_sched_barrier(0);
                     g += 2;
                 }
             }
-            // the remaining full stages (fewer than D) were loaded already; after
-            // the u-th of them only D - 1 - u stages' loads are pending
-            auto tail_stage = [&](auto U) {
-                constexpr int u = decltype(U)::value;
-                if constexpr (u <= D - 2) {  // a tail has at most D - 1 stages
-                    wait_vm<kLPS * (D - 1 - u)>();
-                    if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
-                    step(ring[u], sring[u], pring[u], slot(u), 0, g);
-                    step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
-                    g += 2;
-                }
-            };
-            using I0 = std::integral_constant<int, 0>;
-            using I1 = std::integral_constant<int, 1>;
-            using I2 = std::integral_constant<int, 2>;
-            switch (full - nblocks * D) {
-                case 1: tail_stage(I0{}); break;
-                case 2: tail_stage(I0{}); tail_stage(I1{}); break;
-                case 3: tail_stage(I0{}); tail_stage(I1{}); tail_stage(I2{}); break;
-                default: break;
+        };
+        if (full >= D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) load_stage(XLc, g_begin + 2 * u, ring[u], sring[u], pring[u], slot(u), false);
+            scales_ready(std::integral_constant<int, kLPS * D>{});
+            const int pre = full - D;  // stages followed by a prefetch
+            const int nblocks = pre / D;
+            for (int blk = 0; blk < nblocks; ++blk) {
+                prefetching(I0{});
+                prefetching(I1{});
+                if constexpr (D > 2) prefetching(I2{});
+                if constexpr (D > 3) prefetching(I3{});
+            }
+            const int r = pre - nblocks * D;
+            final_one(I0{}, r);
+            final_one(I1{}, r);
+            final_one(I2{}, r);
+            final_one(I3{}, r);
+            after_one(I0{}, r);
+            after_one(I1{}, r);
+            after_one(I2{}, r);
+        } else {
+            // fewer full stages than the ring holds (short slices of small K)
+            switch (full) {
+                case 1:
+                    load_stage(XLc, g_begin, ring[0], sring[0], pring[0], slot(0), false);
+                    scales_ready(I0{});
+                    last(I0{}, I1{});
+                    break;
+                case 2:
+                    if constexpr (D > 2) {
+                        load_stage(XLc, g_begin, ring[0], sring[0], pring[0], slot(0), false);
+                        load_stage(XLc, g_begin + 2, ring[1], sring[1], pring[1], slot(1), false);
+                        scales_ready(I0{});
+                        last(I0{}, I2{});
+                    }
+                    break;
+                case 3:
+                    if constexpr (D > 3) {
+                        load_stage(XLc, g_begin, ring[0], sring[0], pring[0], slot(0), false);
+                        load_stage(XLc, g_begin + 2, ring[1], sring[1], pring[1], slot(1), false);
+                        load_stage(XLc, g_begin + 4, ring[2], sring[2], pring[2], slot(2), false);
+                        scales_ready(I0{});
+                        last(I0{}, I3{});
+                    }
+                    break;
+                default: scales_ready(I0{}); break;
             }
         }
         if (odd) {
@@ -454,9 +525,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     }
 
     // Left fold of the 8 slice sums, ((((((s0 + s1) + s2) + s3) + s4) + s5) + s6) + s7,
-    // shared by the waves.  Each wave waits for its own loads (the prefetches
-    // past its slice's end still write into its ring regions), then writes its
-    // slice sum into its own regions of ring slots 0 and 1 (values 16 tt + v,
+    // shared by the waves.  Each wave's loads have all landed (the wait below
+    // only guards that: its direct loads write its ring regions), then it writes
+    // its slice sum into its own regions of ring slots 0 and 1 (values 16 tt + v,
     // the first NT * 8 in slot 0, the rest in slot 1), so only one barrier
     // stands between the last wave's finish and the fold; then wave w folds
     // and stores values V = w, w + 8, ... (V = 16 tt + v) of every lane.
