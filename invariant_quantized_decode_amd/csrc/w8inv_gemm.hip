@@ -156,10 +156,13 @@ __device__ __forceinline__ void wait_vm() {
 // PK: W and S are in the packed layout (w8_pack): each stage's weights are two
 // contiguous 1 KB blocks already in the matrix-core lane order, and its scales
 // one 128-byte line, loaded with the stage.
+// R: output rows per workgroup (8..32; 32 with the SwiGLU epilogue).  The
+// matrix core always computes 32 rows; rows R..31 repeat row R - 1's loads
+// (no extra memory traffic) and are not stored.
 template <int TP16, int D, bool LS, int EPI, bool PK>  // TP16 = T_pad / 16 (1..4), D = ring depth (2..4)
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, LinearEpilogue ep) {
+    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, LinearEpilogue ep, int R) {
     static_assert(TP16 >= 1 && TP16 <= 4, "T_pad 16..64");
     static_assert(D >= 2 && D <= 4, "ring depth");
     constexpr int NT = (TP16 + 1) / 2;                // 32-column tiles
@@ -181,8 +184,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = (int)(K / kGroup);
-    const int64_t n0 = (int64_t)blockIdx.x * kRows;
-    // The workgroup's 32 rows: n0 .. n0 + 31, or with the SwiGLU epilogue the
+    const int64_t n0 = (int64_t)blockIdx.x * R;
+    // The workgroup's rows: n0 .. n0 + R - 1, or with the SwiGLU epilogue the
     // 16 gate rows h0 .. h0 + 15 followed by the 16 matching up rows
     // F + h0 .. F + h0 + 15.  Rows past the end read the last valid row (valid
     // memory; their results are never stored).
@@ -192,7 +195,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
             const int64_t h = h0 + (rho & 15);
             return (rho < 16 ? 0 : ep.F) + (h < ep.F ? h : ep.F - 1);
         } else {
-            return n0 + rho < N ? n0 + rho : N - 1;
+            const int64_t n = n0 + (rho < R ? rho : R - 1);
+            return n < N ? n : N - 1;
         }
     };
     const int g_begin = __builtin_amdgcn_readfirstlane((int)kslice_begin(G, wave));
@@ -563,9 +567,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         } else if constexpr (EPI == kEpiAdd) {
             // the residual element is read before its own output is written
             // (y may be the residual itself)
-            if (n < N && j < t) Y[(int64_t)j * ldy + n] = add_bf16(b, ep.r[(int64_t)j * ep.ldr + n]);
+            if (r < R && n < N && j < t) Y[(int64_t)j * ldy + n] = add_bf16(b, ep.r[(int64_t)j * ep.ldr + n]);
         } else {
-            if (n < N && j < t) Y[(int64_t)j * ldy + n] = b;
+            if (r < R && n < N && j < t) Y[(int64_t)j * ldy + n] = b;
         }
     }
 }
@@ -908,7 +912,21 @@ struct LinearPlan {
     int depth;        // ring depth of the LDS-staged split kernel
     bool lds_scales;  // ... and whether it copies the scales to LDS; for the
                       // tiles kernel: whether it loads the scales by blocks
+    int rows = kRows; // output rows per workgroup of the split kernel
 };
+
+// Plain layout: rows per workgroup so that the workgroups cover every CU
+// where 32-row ones would not (N < 256 x 32): ceil(N / 256) rounded up to a
+// multiple of 8 (a whole 128-byte line of the packed layout's rows; the
+// plain layout's loads are by row anyway).  The packed layout keeps 32: its
+// stream reaches the HBM rate from 192 CUs and more workgroups only added
+// contention (6144x5120 t = 1: 9.1 -> 9.9 us), while the plain layout gained
+// on every shape (6144x5120 t = 32: 16.7 -> 15.6 us, 1024x5120 T_pad 16:
+// 12.8 -> 9.9 us).
+static int plain_rows_per_workgroup(int64_t N) {
+    const int64_t need = (N + 255) / 256;
+    return need >= kRows ? kRows : (int)((need + 7) / 8 * 8);
+}
 
 // The LDS-staged variant: the deepest ring (3 or 2 stages for one 32-column
 // tile, 2 for two) whose LDS leaves room for the strip's scales when they can
@@ -935,7 +953,9 @@ static LinearPlan plan_linear(int64_t N, int64_t K, int T_pad, const void* S) {
         const bool sc = (K / kGroup) % 8 == 0 && s16;
         return {LinearKernel::kTiles, tp16, 0, sc};
     }
-    return plan_split(tp16, s16 ? round_dma(64 * (K / kGroup)) : 0);
+    LinearPlan p = plan_split(tp16, s16 ? round_dma(64 * (K / kGroup)) : 0);
+    p.rows = plain_rows_per_workgroup(N);
+    return p;
 }
 
 // SwiGLU rows: two scale blocks of 32 G bytes; the up rows' block starts at
@@ -944,7 +964,9 @@ static LinearPlan plan_epilogue(int epi, int64_t N, int64_t K, int T_pad, const 
     const int64_t G = K / kGroup;
     const bool s16 = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
     if (epi == kEpiSwiGLU) return plan_split(T_pad / 16, s16 && ((N / 2) * G) % 8 == 0 ? 2 * round_dma(32 * G) : 0);
-    return plan_split(T_pad / 16, s16 ? round_dma(64 * G) : 0);
+    LinearPlan p = plan_split(T_pad / 16, s16 ? round_dma(64 * G) : 0);
+    p.rows = plain_rows_per_workgroup(N);
+    return p;
 }
 
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S) {
@@ -1000,14 +1022,15 @@ template <int EPI, bool PK = false>
 static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
                         uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                         hipStream_t stream) {
-    const int64_t wgs = EPI == kEpiSwiGLU ? (ep.F + kRows / 2 - 1) / (kRows / 2) : (N + kRows - 1) / kRows;
+    const int R = EPI == kEpiSwiGLU ? kRows : p.rows;
+    const int64_t wgs = EPI == kEpiSwiGLU ? (ep.F + kRows / 2 - 1) / (kRows / 2) : (N + R - 1) / R;
     const dim3 grid((unsigned)wgs);
     const dim3 block(kGemmThreads);
 #define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                     \
     case TP * 16 + D * 2 + LS:                                                                          \
         if constexpr (!(PK && LS))                                                                      \
             hipLaunchKernelGGL((gemm_w8g32_split_lds<TP, D, LS, EPI, PK>), grid, block, 0, stream, W, S, X, Y, N, \
-                               K, t, ldx, ldy, ep);                                                     \
+                               K, t, ldx, ldy, ep, R);                                                  \
         break;
     switch (p.tp16 * 16 + p.depth * 2 + (p.lds_scales ? 1 : 0)) {
         W8I_SPLIT_LAUNCH(1, 2, true)
