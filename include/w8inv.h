@@ -66,6 +66,8 @@ const char *w8i_version(void);
  *          16-byte aligned, ldx >= K, ldx % 8 == 0.
  *   y      bf16  [t, ldy] row-major: token j's N outputs are contiguous;
  *          2-byte aligned, ldy >= N.  Only y[j, n] with j < t, n < N is written.
+ *          y must not overlap W_q, scales or x: other workgroups still read
+ *          them while y is written (not checked).
  *   t      real columns, 0 <= t <= T_pad.
  *   T_pad  fixed decode width: 16, 32, 48 or 64.  The kernel computes all
  *          T_pad columns (the first ones real, the rest zero) for every t.
