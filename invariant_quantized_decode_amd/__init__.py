@@ -74,7 +74,8 @@ def _load():
     L.w8i_exp32.argtypes = [P, P, I64, P]
     L.w8i_log32.argtypes = [P, P, I64, P]
     for name in ("w8_linear_add_invariant", "w8_linear_swiglu_invariant", "w8_pack_bytes", "w8_pack",
-                 "w8_linear_invariant_packed", "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed", "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
+                 "w8_linear_invariant_packed", "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed",
+                 "w8i_rmsnorm", "w8i_swiglu", "w8i_residual_add", "w8i_exp32", "w8i_log32"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -91,8 +92,11 @@ def _check(fn: str, status: int):
         raise W8InvError(fn, status)
 
 
-def _stream(device) -> int:
-    return torch.cuda.current_stream(device).cuda_stream
+def _launch(fn, device, *args):
+    """Call library function `fn` with `device` current and its current stream as the last argument
+    (HIP launches on a stream of the current device; the library also sizes some grids from it)."""
+    with torch.cuda.device(device):
+        return fn(*args, ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream))
 
 
 def _ptr(t):
@@ -155,8 +159,8 @@ def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor
     W_q int8 [N, K]; scales fp16 [N, K/32]; x bf16 [>=t, K] (token rows); y bf16 [t, N] (allocated if None).
     """
     N, K, ldx, y, ldy = _projection_args(W_q, scales, x, t, y, W_q.shape[0])
-    st = _lib.w8_linear_invariant(_ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y), N, K, ldx, ldy,
-                                  None, 0, ctypes.c_void_p(_stream(W_q.device)))
+    st = _launch(_lib.w8_linear_invariant, W_q.device, _ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y),
+                 N, K, ldx, ldy, None, 0)
     _check("w8_linear_invariant", st)
     return y
 
@@ -168,9 +172,8 @@ def w8_linear_add_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Te
     _same_gpu(("W_q", W_q), ("residual", residual))
     if residual.dtype != torch.bfloat16 or residual.dim() != 2 or residual.size(1) != N or residual.size(0) < t:
         raise ValueError("residual must be a bf16 [>=t, N] tensor")
-    st = _lib.w8_linear_add_invariant(_ptr(W_q), _ptr(scales), _ptr(x), _ptr(residual), int(t), int(T_pad), _ptr(y),
-                                      N, K, ldx, _row_major(residual, "residual"), ldy,
-                                      ctypes.c_void_p(_stream(W_q.device)))
+    st = _launch(_lib.w8_linear_add_invariant, W_q.device, _ptr(W_q), _ptr(scales), _ptr(x), _ptr(residual), int(t),
+                 int(T_pad), _ptr(y), N, K, ldx, _row_major(residual, "residual"), ldy)
     _check("w8_linear_add_invariant", st)
     return y
 
@@ -182,8 +185,8 @@ def w8_linear_swiglu_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch
         raise ValueError("W_q must be [2F, K]")
     F = W_q.shape[0] // 2
     N, K, ldx, y, ldy = _projection_args(W_q, scales, x, t, y, F)
-    st = _lib.w8_linear_swiglu_invariant(_ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y), F, K, ldx,
-                                         ldy, ctypes.c_void_p(_stream(W_q.device)))
+    st = _launch(_lib.w8_linear_swiglu_invariant, W_q.device, _ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad),
+                 _ptr(y), F, K, ldx, ldy)
     _check("w8_linear_swiglu_invariant", st)
     return y
 
@@ -207,8 +210,7 @@ def w8_pack(W_q: torch.Tensor, scales: torch.Tensor) -> tuple[torch.Tensor, torc
     wb, sb = w8_pack_bytes(N, K)
     Wp = torch.empty(wb, dtype=torch.int8, device=W_q.device)
     Sp = torch.empty(sb // 2, dtype=torch.int16, device=W_q.device)
-    _check("w8_pack", _lib.w8_pack(_ptr(W_q), _ptr(scales), N, K, _ptr(Wp), _ptr(Sp),
-                                   ctypes.c_void_p(_stream(W_q.device))))
+    _check("w8_pack", _launch(_lib.w8_pack, W_q.device, _ptr(W_q), _ptr(scales), N, K, _ptr(Wp), _ptr(Sp)))
     return Wp, Sp
 
 
@@ -234,9 +236,8 @@ def w8_linear_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tens
                                y: torch.Tensor | None = None) -> torch.Tensor:
     """w8_linear_invariant over the packed layout from w8_pack (same bits).  x bf16 [>=t, K]; y bf16 [t, N]."""
     K, y = _packed_args(Wp, Sp, x, t, N, N, y, N)
-    st = _lib.w8_linear_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y), int(N), K,
-                                         _row_major(x, "x"), _row_major(y, "y"),
-                                         ctypes.c_void_p(_stream(Wp.device)))
+    st = _launch(_lib.w8_linear_invariant_packed, Wp.device, _ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y),
+                 int(N), K, _row_major(x, "x"), _row_major(y, "y"))
     _check("w8_linear_invariant_packed", st)
     return y
 
@@ -248,10 +249,9 @@ def w8_linear_add_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.
     _same_gpu(("Wp", Wp), ("residual", residual))
     if residual.dtype != torch.bfloat16 or residual.dim() != 2 or residual.size(1) != N or residual.size(0) < t:
         raise ValueError("residual must be a bf16 [>=t, N] tensor")
-    st = _lib.w8_linear_add_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), _ptr(residual), int(t), int(T_pad),
-                                             _ptr(y), int(N), K, _row_major(x, "x"),
-                                             _row_major(residual, "residual"), _row_major(y, "y"),
-                                             ctypes.c_void_p(_stream(Wp.device)))
+    st = _launch(_lib.w8_linear_add_invariant_packed, Wp.device, _ptr(Wp), _ptr(Sp), _ptr(x), _ptr(residual), int(t),
+                 int(T_pad), _ptr(y), int(N), K, _row_major(x, "x"), _row_major(residual, "residual"),
+                 _row_major(y, "y"))
     _check("w8_linear_add_invariant_packed", st)
     return y
 
@@ -260,9 +260,8 @@ def w8_linear_swiglu_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: tor
                                       F: int, y: torch.Tensor | None = None) -> torch.Tensor:
     """w8_linear_swiglu_invariant over the packed layout of the [2F, K] gate+up projection (same bits)."""
     K, y = _packed_args(Wp, Sp, x, t, F, 2 * F, y, F)
-    st = _lib.w8_linear_swiglu_invariant_packed(_ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y), int(F),
-                                                K, _row_major(x, "x"), _row_major(y, "y"),
-                                                ctypes.c_void_p(_stream(Wp.device)))
+    st = _launch(_lib.w8_linear_swiglu_invariant_packed, Wp.device, _ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad),
+                 _ptr(y), int(F), K, _row_major(x, "x"), _row_major(y, "y"))
     _check("w8_linear_swiglu_invariant_packed", st)
     return y
 
@@ -307,8 +306,8 @@ def vocab_block_logprob(logits: torch.Tensor, targets: torch.Tensor, block: int,
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
     fn = _lib.vocab_block_logprob_direct if direct else _lib.vocab_block_logprob
-    st = fn(_ptr(logits), _ptr(targets), int(block), _ptr(out), t, V, ldl, _ptr(workspace), workspace.numel(),
-            ctypes.c_void_p(_stream(logits.device)))
+    st = _launch(fn, logits.device, _ptr(logits), _ptr(targets), int(block), _ptr(out), t, V, ldl, _ptr(workspace),
+                 workspace.numel())
     _check("vocab_block_logprob_direct" if direct else "vocab_block_logprob", st)
     return out
 
@@ -342,8 +341,8 @@ def vocab_argmax(logits: torch.Tensor, out: torch.Tensor | None = None, t: int |
     _same_gpu(("logits", logits), ("out", out), ("workspace", workspace))
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
-    st = _lib.vocab_argmax(_ptr(logits), _ptr(out), t, V, ldl, _ptr(workspace), workspace.numel(),
-                           ctypes.c_void_p(_stream(logits.device)))
+    st = _launch(_lib.vocab_argmax, logits.device, _ptr(logits), _ptr(out), t, V, ldl, _ptr(workspace),
+                 workspace.numel())
     _check("vocab_argmax", st)
     return out
 
@@ -359,8 +358,7 @@ def w8i_rmsnorm(x: torch.Tensor, eps: float, weight: torch.Tensor | None = None,
         raise ValueError("weight must be a contiguous bf16 [H] tensor")
     if y.shape[0] < t or y.shape[1] != H:
         raise ValueError("y must be bf16 [t, H]")
-    st = _lib.w8i_rmsnorm(_ptr(x), _ptr(weight), float(eps), _ptr(y), t, H, ldx, _row_major(y, "y"),
-                          ctypes.c_void_p(_stream(x.device)))
+    st = _launch(_lib.w8i_rmsnorm, x.device, _ptr(x), _ptr(weight), float(eps), _ptr(y), t, H, ldx, _row_major(y, "y"))
     _check("w8i_rmsnorm", st)
     return y
 
@@ -373,8 +371,8 @@ def w8i_swiglu(gate_up: torch.Tensor, y: torch.Tensor | None = None) -> torch.Te
     _dtype(gate_up, "gate_up", torch.bfloat16), _dtype(y, "y", torch.bfloat16)
     if y.shape[0] < t or y.shape[1] != F:
         raise ValueError("y must be bf16 [t, F]")
-    st = _lib.w8i_swiglu(_ptr(gate_up), _ptr(y), t, F, _row_major(gate_up, "gate_up"), _row_major(y, "y"),
-                         ctypes.c_void_p(_stream(gate_up.device)))
+    st = _launch(_lib.w8i_swiglu, gate_up.device, _ptr(gate_up), _ptr(y), t, F, _row_major(gate_up, "gate_up"),
+                 _row_major(y, "y"))
     _check("w8i_swiglu", st)
     return y
 
@@ -387,8 +385,8 @@ def w8i_residual_add(a: torch.Tensor, b: torch.Tensor, y: torch.Tensor | None = 
         _dtype(ten, name, torch.bfloat16)
         if ten.dim() != 2 or ten.shape[0] < t or ten.shape[1] != H:
             raise ValueError(f"{name} must be bf16 [t, H]")
-    st = _lib.w8i_residual_add(_ptr(a), _ptr(b), _ptr(y), t, H, _row_major(a, "a"), _row_major(b, "b"),
-                               _row_major(y, "y"), ctypes.c_void_p(_stream(a.device)))
+    st = _launch(_lib.w8i_residual_add, a.device, _ptr(a), _ptr(b), _ptr(y), t, H, _row_major(a, "a"),
+                 _row_major(b, "b"), _row_major(y, "y"))
     _check("w8i_residual_add", st)
     return y
 
@@ -400,7 +398,7 @@ def w8i_exp32(x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
     _dtype(x, "x", torch.float32), _dtype(y, "y", torch.float32)
     if y.numel() < x.numel() or not y.is_contiguous():
         raise ValueError("y must be a contiguous fp32 tensor as large as x")
-    _check("w8i_exp32", _lib.w8i_exp32(_ptr(x), _ptr(y), x.numel(), ctypes.c_void_p(_stream(x.device))))
+    _check("w8i_exp32", _launch(_lib.w8i_exp32, x.device, _ptr(x), _ptr(y), x.numel()))
     return y
 
 
@@ -411,7 +409,7 @@ def w8i_log32(x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
     _dtype(x, "x", torch.float32), _dtype(y, "y", torch.float32)
     if y.numel() < x.numel() or not y.is_contiguous():
         raise ValueError("y must be a contiguous fp32 tensor as large as x")
-    _check("w8i_log32", _lib.w8i_log32(_ptr(x), _ptr(y), x.numel(), ctypes.c_void_p(_stream(x.device))))
+    _check("w8i_log32", _launch(_lib.w8i_log32, x.device, _ptr(x), _ptr(y), x.numel()))
     return y
 
 
