@@ -7,9 +7,10 @@
  *    the storage of torch tensors).  The library never allocates, frees or
  *    keeps a pointer after the call returns.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
- *    null stream).  Nothing synchronises: the return value is the result of
- *    host-side argument validation and of the launch itself, not of the
- *    kernels' execution.
+ *    null stream), which must belong to the calling thread's current device,
+ *    as the pointers must.  Nothing synchronises: the return value is the
+ *    result of host-side argument validation and of the launch itself, not
+ *    of the kernels' execution.
  *  - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
  *  - A call with t == 0 (or n == 0) validates nothing else, launches nothing
  *    and returns W8I_OK.
