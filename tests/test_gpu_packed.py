@@ -20,7 +20,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import invariant_quantized_decode_amd as w8  # noqa: E402
-from tests.gpu_util import bf16, bits, f16, i8, say  # noqa: E402
+from tests.gpu_util import DEV, bf16, bits, f16, i8, say  # noqa: E402
 
 
 def layout(q, s):
@@ -133,3 +133,33 @@ def test_packed_projection_matches_oracle():
     ok, err = within_bf16_ulps(y, oracle.w8_linear(q, s, x), 2.0)
     say(f"packed vs oracle: max err {float(err.max()):.3f} ulp")
     assert ok.all()
+
+
+@pytest.mark.parametrize("N,K,T_pad", [(1000, 2080, 32), (257, 544, 64), (131172, 1024, 32)])
+def test_strided_activations_and_outputs(N, K, T_pad):
+    """x read from inside a wider buffer (ldx > K, rows offset by 16 bytes) and y written into a wider
+    one (ldy > N, an odd element offset): the contiguous call's bits, and nothing written outside y's
+    window.  Plain and packed layouts; the last shape runs the persistent kernel."""
+    say(f"case strided N={N} K={K} T_pad={T_pad}")
+    rng = np.random.default_rng(N + 5 * K)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    x = synth.draw_acts(rng, T_pad, K)
+    Wd, Sd = i8(q), f16(s)
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    t = T_pad - 3
+    want = bits(w8.w8_linear_invariant(Wd, Sd, bf16(x[:t]), t, T_pad))
+    xw = torch.zeros((t, K + 72), dtype=torch.bfloat16, device=DEV)
+    xw[:, 8:8 + K] = bf16(x[:t])
+    xs = xw[:, 8:8 + K]
+    for packed in (False, True):
+        yw = torch.full((t + 1, N + 41), -7.0, dtype=torch.bfloat16, device=DEV)
+        ys = yw[:t, 3:3 + N]
+        if packed:
+            w8.w8_linear_invariant_packed(Wp, Sp, xs, t, T_pad, N, y=ys)
+        else:
+            w8.w8_linear_invariant(Wd, Sd, xs, t, T_pad, y=ys)
+        assert np.array_equal(bits(ys), want), f"packed={packed}"
+        outside = torch.ones_like(yw, dtype=torch.bool)
+        outside[:t, 3:3 + N] = False
+        assert bool((yw[outside] == -7.0).all()), f"packed={packed}: written outside y"
