@@ -163,3 +163,29 @@ def test_strided_activations_and_outputs(N, K, T_pad):
         outside = torch.ones_like(yw, dtype=torch.bool)
         outside[:t, 3:3 + N] = False
         assert bool((yw[outside] == -7.0).all()), f"packed={packed}: written outside y"
+
+
+def test_concurrent_streams_give_the_sequential_bits():
+    """The library keeps no state between calls: two projections issued on two streams at once,
+    four times each, give the bits each gives alone."""
+    say("case concurrent streams")
+    rng = np.random.default_rng(99)
+    cases = []
+    for N, K in ((6144, 5120), (1000, 2080)):
+        q = synth.draw_codes(rng, N, K)
+        s = synth.draw_scales(rng, N, K, 0.0)
+        x = synth.draw_acts(rng, 32, K)
+        Wp, Sp = w8.w8_pack(i8(q), f16(s))
+        Xd = bf16(x)
+        alone = bits(w8.w8_linear_invariant_packed(Wp, Sp, Xd, 32, 32, N))
+        cases.append((Wp, Sp, Xd, N, alone))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(4):
+        for (Wp, Sp, Xd, N, _), st in zip(cases, streams):
+            with torch.cuda.stream(st):
+                outs.append((w8.w8_linear_invariant_packed(Wp, Sp, Xd, 32, 32, N), N))
+    torch.cuda.synchronize()
+    for k, (y, N) in enumerate(outs):
+        assert np.array_equal(bits(y), cases[k % 2][4]), f"call {k} on stream {k % 2}"
