@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--all", action="store_true",
                    help="instead of the bench line: one JSON line per workload (every configured projection and "
                         "the chain's, at t=1 and t=T_pad, and the head's logprob), with the CPU oracle on a row sample")
+    p.add_argument("--only", default="",
+                   help="with --all: only the workloads whose name contains this text")
     p.add_argument("--layout", choices=("packed", "plain"), default="packed",
                    help="weight layout of the headline step (the other one is reported beside it)")
     p.add_argument("--pmc-pass", action="store_true",
@@ -287,10 +289,15 @@ def run_all(torch, w8, synth, dev, args):
              ("chain gate+up + SwiGLU (fused) 34816x5120", 34816, 5120, synth.CHAIN_T_PAD, 0.0, "swiglu"),
              ("chain down + residual (fused) 5120x17408", 5120, 17408, synth.CHAIN_T_PAD, 0.0, "add")]
     work += [(n, N, K, T, e, op + "_packed") for n, N, K, T, e, op in list(work) if op in ("add", "swiglu")]
+    def want(workload: str) -> bool:
+        return not args.only or args.only in workload
+
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     stream = torch.cuda.Stream(device=dev)
     for name, N, K, T_pad, eps, op in work:
+        if not want(name + (" [packed]" if op.endswith("packed") else "")):
+            continue
         wbytes = N * K + 2 * N * (K // 32)
         copies = max(1, math.ceil((1 << 30) / wbytes))
         Ws = [torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8, device=dev) for _ in range(copies)]
@@ -366,6 +373,8 @@ def run_all(torch, w8, synth, dev, args):
     for gname, fn, nbytes in (("rmsnorm", lambda: w8.w8i_rmsnorm(xg, 1e-6, y=yh), 2 * 2 * tg * H),
                               ("swiglu", lambda: w8.w8i_swiglu(gu, y=yf), 3 * 2 * tg * F),
                               ("residual add", lambda: w8.w8i_residual_add(xg, xg, y=yh), 3 * 2 * tg * H)):
+        if not want(f"glue {gname} t={tg} H={H} F={F}"):
+            continue
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             fn()
@@ -387,7 +396,9 @@ def run_all(torch, w8, synth, dev, args):
                           "roofline_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
     # the head's logprob epilogue
     V, block = synth.HEAD.N, synth.HEAD_BLOCK
-    for t in (1, synth.HEAD.T_pad):
+    vocab = (f"vocab block logprob V={V} block={block}", f"vocab greedy argmax V={V}",
+             f"vocab block logprob, blockwise-direct V={V}")
+    for t in (1, synth.HEAD.T_pad) if any(want(n) for n in vocab) else ():
         logits = (torch.randn(t, V, generator=g, device=dev) * 105).to(torch.bfloat16)
         targets = torch.randint(0, V, (t,), generator=g, device=dev, dtype=torch.int64)
         ws = torch.empty(w8.vocab_block_logprob_workspace_bytes(t, V, block), dtype=torch.uint8, device=dev)
