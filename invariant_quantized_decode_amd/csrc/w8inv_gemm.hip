@@ -137,6 +137,13 @@ __host__ __device__ constexpr int split_lds_scale_bytes(int NT, int D) {
 __device__ __forceinline__ uint32_t xs_off(int a, int p) { return (uint32_t)(a * 128 + 16 * (p ^ ((a >> 1) & 7))); }
 __device__ __forceinline__ uint32_t xs_piece(int a, int lane) { return (uint32_t)((lane & 7) ^ ((a >> 1) & 7)); }
 
+// Of the nv values a lane holds for 32-column tile tt (value v: column
+// 32 tt + 8 (v / 4) + 4 (lane / 32) + v % 4, i.e. column group 4 tt + v / 4),
+// the leading ones that fall in the first xl groups of 8 columns.
+__device__ __forceinline__ constexpr int tile_live_values(int tt, int xl, int nv) {
+    return 4 * (xl - 4 * tt) <= 0 ? 0 : 4 * (xl - 4 * tt) < nv ? 4 * (xl - 4 * tt) : nv;
+}
+
 // Byte offset given to the activation loads of padding columns (j >= t): past
 // the end of any activation buffer (t <= 64 rows of at most 2^24 bf16 is at
 // most 2^31 bytes), so the buffer descriptor's range check returns zeros and
@@ -311,21 +318,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
             __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, W8I_LDS(xs + wave * kStageBytes + i * kLdsDmaBytes), 16,
                                                      xd_off[i], g * (2 * kGroup), 0, 0);
     };
-    // group gs of the stage (weights already swapped), acc += s * D_g in fp64
-    auto step = [&](const u32x4 (&w)[2], const uint16_t (&ss)[2], uint32_t sp, const unsigned char* xs, int gs,
-                    int g) {
+    // group gs of the stage (weights already swapped), acc += s * D_g in fp64,
+    // for the values of the column groups below XL = XLc (value v of tile tt
+    // holds columns of group 4 tt + v / 4); the other values are padding
+    // columns, never stored, so their products are not formed, and a tile
+    // with no live value is skipped whole
+    auto step = [&](auto XLc, const u32x4 (&w)[2], const uint16_t (&ss)[2], uint32_t sp, const unsigned char* xs,
+                    int gs, int g) {
+        constexpr int XL = decltype(XLc)::value;
         const bf16x8 b_lo = dequant8(w[gs].x, w[gs].y);
         const bf16x8 b_hi = dequant8(w[gs].z, w[gs].w);
         const uint16_t s16 = PK ? (uint16_t)(sp >> (16 * gs)) : LS ? s_lds[s_row_lds + g] : ss[gs];
         const double sc = (double)(float)__builtin_bit_cast(_Float16, s16);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
+            const int nv = tile_live_values(tt, XL, (tt == NT - 1) ? kLastValues : 16);
+            if (nv == 0) continue;
             const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + xa_off[tt][gs][0]);
             const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + xa_off[tt][gs][1]);
             const f32x16 zero = {};
             f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo, zero, 0, 0, 0);
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0, 0);
-            const int nv = (tt == NT - 1) ? kLastValues : 16;
 #pragma unroll
             for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc, (double)d[v], acc[tt][v]);
         }
@@ -378,8 +391,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         auto compute = [&](auto U) {
             constexpr int u = decltype(U)::value;
             if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
-            step(ring[u], sring[u], pring[u], slot(u), 0, g);
-            step(ring[u], sring[u], pring[u], slot(u), 1, g + 1);
+            step(XLc, ring[u], sring[u], pring[u], slot(u), 0, g);
+            step(XLc, ring[u], sring[u], pring[u], slot(u), 1, g + 1);
         };
         // Only real stages are loaded: the first min(D, full) up front, then
         // stage q + D right after stage q is computed, while q + D < full.
@@ -507,13 +520,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
             load_stage(XLc, g_end - 1, w1, s1, p1, xr0, true);
             wait_vm<0>();
             if constexpr (!PK) swap16(w1[0], w1[1]);
-            step(w1, s1, p1, xr0, 0, g_end - 1);
+            step(XLc, w1, s1, p1, xr0, 0, g_end - 1);
         }
     };
     // one uniform branch per launch: XL = the column groups holding a live
     // column, rounded up to 1, 2, 4 or all
+    const int live_groups = (t + 7) / 8;
     {
-        const int live_groups = (t + 7) / 8;
         if (live_groups <= 1) {
             run(std::integral_constant<int, 1>{});
         } else if (live_groups <= 2) {
@@ -540,17 +553,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         constexpr int kHalf = NT * 8;
         return reinterpret_cast<double*>((V < kHalf ? xr0 : xr1) + w * kStageBytes) + (V % kHalf) * 64 + lane;
     };
+    // (only values of live column groups: the others were not computed)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) *part(wave, tt * 16 + v) = acc[tt][v];
+        for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v)
+            if (4 * tt + (v >> 2) < live_groups) *part(wave, tt * 16 + v) = acc[tt][v];
     __syncthreads();
     const int64_t n = n0 + r;
 #pragma unroll
     for (int k = 0; k < 2 * NT; ++k) {
         const int V = wave + kKSlices * k;
         const int tt = V >> 4, v = V & 15;
-        if (v >= ((tt == NT - 1) ? kLastValues : 16)) continue;
+        if (v >= ((tt == NT - 1) ? kLastValues : 16) || 4 * tt + (v >> 2) >= live_groups) continue;
         double sum = *part(0, V);
 #pragma unroll
         for (int w = 1; w < kKSlices; ++w) sum = sum + *part(w, V);
@@ -751,8 +766,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // computed for live columns does not depend on XL).  The plain layout's
     // 4-stage blocks give a stage's column groups to two waves, so it always
     // loads them all.
+    // Only the values of the first XG column groups of 8 are computed (with
+    // the packed layout the XL groups loaded, otherwise all): the others are
+    // padding columns, never stored.
     auto run = [&](auto XLc) {
         constexpr int XL = decltype(XLc)::value;
+        constexpr int XG = PK ? XL : 4 * NT;
         if constexpr (XL < kXLoads) {
 #pragma unroll
             for (int i = XL; i < kXLoads; ++i) {
@@ -819,6 +838,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                         const double scale = (double)(float)__builtin_bit_cast(_Float16, s16);
 #pragma unroll
                         for (int tt = 0; tt < NT; ++tt) {
+                            const int nv = tile_live_values(tt, XG, (tt == NT - 1) ? kLastValues : 16);
+                            if (nv == 0) continue;
                             const unsigned char* xt = xs + u * kStageBytes + tt * kXTileBytes;
                             const u32x4 a0 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c));
                             const u32x4 a1 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c + 1));
@@ -827,7 +848,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                                                                                zero, 0, 0, 0);
                             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0,
                                                                         0);
-                            const int nv = (tt == NT - 1) ? kLastValues : 16;
 #pragma unroll
                             for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(scale, (double)d[v], acc[tt][v]);
                         }
