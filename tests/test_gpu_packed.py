@@ -102,8 +102,9 @@ def test_packed_persistent_kernel_gives_the_plain_bits(N, K, T_pad):
 
 @pytest.mark.parametrize("N,K,T_pad", [(1000, 1056, 64), (300, 2080, 32), (70, 544, 16), (131172, 1024, 32)])
 def test_skipped_padding_loads_keep_the_bits(N, K, T_pad):
-    """Activation loads whose 8 columns are all padding are not issued; the kernels pick 1, 2, 4
-    or all column groups per launch.  On both sides of every such boundary (t = 8, 9, 16, 17,
+    """Activation loads whose 8 columns are all padding are not issued, nor are those columns'
+    products formed (a tile with no live column skips its MFMAs); the kernels pick 1, 2, 4 or all
+    column groups per launch.  On both sides of every such boundary (t = 8, 9, 16, 17,
     32, 33) each column keeps the bits it has at full width, on both layouts and in both kernels
     (the last case runs the persistent one)."""
     say(f"case padding loads N={N} K={K} T_pad={T_pad}")
