@@ -103,20 +103,26 @@ def test_linear_swiglu_equals_linear_then_swiglu(F, K, t, T_pad, aligned):
     assert np.array_equal(got, want)
 
 
-def test_fused_columns_are_t_invariant():
-    """Column 0's bits do not depend on t or on the other columns (the pages' fixed-width contract)."""
-    rng, q, s, x = draw(9, 2 * 96, 1024, 32)
-    res = synth.draw_acts(rng, 32, 2 * 96)
+@pytest.mark.parametrize("T_pad", [32, 64])
+def test_fused_columns_are_t_invariant(T_pad):
+    """A column's bits do not depend on t or on the other columns (the pages' fixed-width contract),
+    on both layouts; at T_pad 64 the t <= 32 cases leave the second 32-column tile without a live
+    column (its products are skipped)."""
+    rng, q, s, x = draw(9 + T_pad, 2 * 96, 1024, T_pad)
+    res = synth.draw_acts(rng, T_pad, 2 * 96)
     Wd, Sd, Xd, Rd = i8(q), f16(s), bf16(x), bf16(res)
-    full_sw = bits(w8.w8_linear_swiglu_invariant(Wd, Sd, Xd, 32, 32))
-    full_add = bits(w8.w8_linear_add_invariant(Wd, Sd, Xd, Rd, 32, 32))
-    for t in (1, 5, 17, 31):
-        perm = rng.permutation(32)[:t]
-        say(f"case fused t={t}")
-        sw = bits(w8.w8_linear_swiglu_invariant(Wd, Sd, bf16(x[perm]), t, 32))
-        ad = bits(w8.w8_linear_add_invariant(Wd, Sd, bf16(x[perm]), bf16(res[perm]), t, 32))
-        assert np.array_equal(sw, full_sw[perm])
-        assert np.array_equal(ad, full_add[perm])
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    full_sw = bits(w8.w8_linear_swiglu_invariant(Wd, Sd, Xd, T_pad, T_pad))
+    full_add = bits(w8.w8_linear_add_invariant(Wd, Sd, Xd, Rd, T_pad, T_pad))
+    for t in (t for t in (1, 5, 9, 17, 31, 33, 63) if t < T_pad):
+        perm = rng.permutation(T_pad)[:t]
+        say(f"case fused T_pad={T_pad} t={t}")
+        xp, rp = bf16(x[perm]), bf16(res[perm])
+        assert np.array_equal(bits(w8.w8_linear_swiglu_invariant(Wd, Sd, xp, t, T_pad)), full_sw[perm])
+        assert np.array_equal(bits(w8.w8_linear_add_invariant(Wd, Sd, xp, rp, t, T_pad)), full_add[perm])
+        assert np.array_equal(bits(w8.w8_linear_swiglu_invariant_packed(Wp, Sp, xp, t, T_pad, 96)), full_sw[perm])
+        assert np.array_equal(bits(w8.w8_linear_add_invariant_packed(Wp, Sp, xp, rp, t, T_pad, 2 * 96)),
+                              full_add[perm])
 
 
 @pytest.mark.parametrize("N,K,t,T_pad", ADD)
