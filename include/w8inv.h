@@ -88,9 +88,12 @@ const char *w8i_version(void);
  *     (an empty slice is +0) and the 8 slice sums are combined by the left
  *     fold ((((((s0+s1)+s2)+s3)+s4)+s5)+s6)+s7.  The plan depends on K only;
  *   - the fp64 result is rounded once to bf16, nearest-even.
- *   No atomics, no autotuning, no arithmetic chosen from t (t only sets how
- *   many activation loads a stage issues: loads of 8 padding columns are
- *   skipped, their columns computed on zeros as before).
+ *   No atomics, no autotuning, no arithmetic of a live column chosen from t.
+ *   t only sets how much padding work is skipped: activation loads whose 8
+ *   columns are all padding are not issued (their LDS regions hold zeros),
+ *   and the products of such padding columns are not formed (a 32-column
+ *   tile with no live column skips its matrix-core steps).  Every live
+ *   column's MFMAs, fp64 sums and rounding are the same for every t.
  *
  * workspace: this kernel needs none; the size query returns 0 and workspace
  * may be NULL.

@@ -413,11 +413,36 @@ def w8i_log32(x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
     return y
 
 
+def _code_only(src: str) -> str:
+    """C++ source without comments, whitespace runs collapsed (string and character literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
-    """SHA-256 over the GEMM kernel's sources: identifies which kernel a stored counter profile measured."""
+    """SHA-256 over the GEMM kernel's code (its sources without comments or layout): identifies which
+    kernel a stored counter profile measured."""
     import hashlib
     h = hashlib.sha256()
     for name in ("w8inv_gemm.hip", "w8inv_math.h", "w8inv_internal.h"):
-        with open(os.path.join(_HERE, "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(_HERE, "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]

@@ -34,12 +34,13 @@
 //    zero; int8 -> bf16 is exact (7 significant bits).
 //  * The fp16 group scale is applied to that fp32 group sum in fp64 (the
 //    product is exact there); the fp64 result is rounded once to bf16.
-//  * Every one of the T_pad columns goes through the matrix core for every t;
-//    columns >= t are zeros and are never stored.  A padding column inside a
+//  * Columns >= t are zeros and are never stored.  A padding column inside a
 //    direct load's 8 columns loads as zeros without a memory access (an
 //    offset past the activation buffer's range); a load whose 8 columns are
-//    all padding is not issued at all, its LDS region zeroed once (the one
-//    thing t selects: how many activation loads a stage issues).
+//    all padding is not issued at all, its LDS region zeroed once, and the
+//    fp64 products of such columns are not formed (a 32-column tile with no
+//    live column skips its MFMAs).  That is all t selects: how much padding
+//    work is skipped, in groups of 8 columns.
 //  * No atomics; the arithmetic of a column -- K plan, MFMA sequence,
 //    roundings -- depends on neither t, its neighbours, N nor the device.
 #include <hip/hip_runtime.h>
@@ -352,7 +353,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     // stored).  What is computed for the live columns -- the K plan, every
     // MFMA and every rounding -- does not depend on XL; the choice only
     // spares the memory pipeline 1 KB per skipped load (at t = 1, three of
-    // every four activation loads).
+    // every four activation loads) and the VALU the padding columns'
+    // products (in `step`).
     auto run = [&](auto XLc) {
         constexpr int XL = decltype(XLc)::value;
         constexpr int kLPS = 2 + XL + (PK ? 1 : LS ? 0 : 2);  // loads per stage

@@ -223,3 +223,15 @@ def test_calibration_library_exports_its_header_and_validates():
     assert C.w8c_mfma_bf16(1, 0, fake, 1024, None) == -2
     assert C.w8c_mfma_bf16(0, 1, fake, 1024, None) == -2
     assert C.w8c_mfma_bf16(2, 1, fake, 1024, None) == -6
+
+
+def test_kernel_digest_follows_code_not_comments():
+    """The digest that ties a stored counter profile to the kernel it measured ignores comments and
+    layout but not code (string and character literals included)."""
+    import invariant_quantized_decode_amd as w8
+    a = 'int f(int x) { return x + 1; } // one\n'
+    assert w8._code_only(a) == w8._code_only('/* doc */ int f(int x)\n{\n    return x + 1;  // two\n}\n')
+    assert w8._code_only(a) != w8._code_only('int f(int x) { return x + 2; }')
+    assert w8._code_only('s = "a // b";') == 's = "a // b";'
+    assert w8._code_only("c = '/'; /* x */ d = '\\''; // y") == "c = '/'; d = '\\'';"
+    assert re.fullmatch(r"[0-9a-f]{16}", w8.kernel_source_digest())
