@@ -88,3 +88,35 @@ def test_packed_full_size_linear(index):
 def test_packed_full_size_head():
     d = synth.head_logprob()
     check("head 248320x5120", d["q"], d["s"], d["pool"], 32, np.random.default_rng(7))
+
+
+def test_largest_accepted_shape():
+    """The largest weights either layout accepts (codes just below 2^32 bytes: the buffer ranges and
+    32-bit offsets the kernels use): 524287 x 8192 on the plain layout (one row short of 2^32
+    bytes, a ragged last strip) and its first 524256 rows (16383 strips) packed.  Sampled rows --
+    the last ones, whose offsets come within 8 KB of 2^32, among them -- are within 2 bf16 ulps of
+    the oracle at T_pad 32 (the persistent kernel) and 64 (the split kernel), the packed rows give
+    the plain bits, and a column keeps its bits at t = 1."""
+    N, K, Np = 524287, 8192, 524256
+    assert N * K < 1 << 32 <= (N + 1) * K and Np // 32 * (K // 64) * 2048 < 1 << 32
+    rng = np.random.default_rng(4242)
+    q = synth.draw_codes(rng, N, K)
+    s = synth.draw_scales(rng, N, K, 0.0)
+    x = synth.draw_acts(rng, 64, K)
+    Wd, Sd, Xd = i8(q), f16(s), bf16(x)
+    Wp, Sp = w8.w8_pack(Wd[:Np], Sd[:Np])
+    rows = np.unique(np.concatenate([[0, Np - 1, Np], np.arange(N - 8, N), rng.choice(N, size=24, replace=False)]))
+    for T_pad in (32, 64):
+        t = T_pad
+        say(f"case largest shape {N}x{K} T_pad={T_pad} ({w8.w8_linear_invariant_kernel(N, K, T_pad)}, "
+            f"packed {w8.w8_linear_invariant_packed_kernel(Np, K, T_pad)})")
+        y = bits(w8.w8_linear_invariant(Wd, Sd, Xd[:t], t, T_pad))
+        ok, err = within_bf16_ulps(y[:, rows], oracle.w8_linear(q, s, x[:t], rows=rows), 2.0)
+        say(f"largest shape T_pad={T_pad}: max err {float(err.max()):.3f} ulp over {ok.size} sampled outputs")
+        assert ok.all()
+        yp = bits(w8.w8_linear_invariant_packed(Wp, Sp, Xd[:t], t, T_pad, Np))
+        assert np.array_equal(yp, y[:, :Np]), f"T_pad={T_pad}: packed rows differ from the plain bits"
+        y1 = bits(w8.w8_linear_invariant(Wd, Sd, Xd[:1], 1, T_pad))
+        assert np.array_equal(y1, y[:1]), f"T_pad={T_pad}: column 0 changed bits at t=1"
+    del Wd, Sd, Wp, Sp
+    torch.cuda.empty_cache()
