@@ -222,7 +222,8 @@ def main():
         cpu = dict(value=round(reps * wbytes / el / 1e9, 4), unit="GB/s", cores=oracle.max_threads(),
                    kind="oracle",
                    sample=f"fp64 oracle on the full {N}x{K} projection at t={T_pad}, {reps} repetitions "
-                          f"in {el:.1f} s")
+                          f"in {el:.1f} s",
+                   host_cpus=len(os.sched_getaffinity(0)), cpu_model=cpu_model())
 
     def r(v, n=3):
         return round(v, n)
@@ -267,8 +268,27 @@ def main():
         },
         "roofline": roof,
         "cpu_baseline": cpu,
+        "inputs_sha256": {"codes": sha256_16(q), "scales": sha256_16(s), "activations": sha256_16(pool)},
     }
     print(json.dumps(line), flush=True)
+
+
+def sha256_16(a) -> str:
+    """First 16 hex digits of the SHA-256 of an array's bytes (C order): identifies the synthetic inputs."""
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def run_all(torch, w8, synth, dev, args):
