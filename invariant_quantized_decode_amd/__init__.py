@@ -7,8 +7,8 @@ step of the computation runs in the library's HIP kernels.  There is no other
 implementation behind these names: if the library is missing, importing this
 package raises.
 
-Storage formats: int8 weight codes; fp16 scales (torch.float16, or int16/uint16
-bit patterns); bf16 activations and logits (torch.bfloat16); int64 targets.
+Storage formats: int8 weight codes; fp16 scales (torch.float16, or their bit
+patterns as torch.int16); bf16 activations and logits (torch.bfloat16); int64 targets.
 """
 from __future__ import annotations
 
