@@ -166,3 +166,36 @@ def test_vocab_head_and_logprob_workload():
         assert np.array_equal(y, base[cols]), f"logits changed bits at t={t}"
         lp = host(w8.vocab_block_logprob(yd, torch.from_numpy(targets[cols]).to(DEV), 4096))
         assert np.array_equal(f32bits(lp), f32bits(lp_base[cols])), f"logprob changed bits at t={t}"
+
+
+def test_degenerate_and_largest_vocabularies():
+    """A one-entry vocabulary, a last block of one entry, and the largest vocabulary the ABI accepts
+    (V = 2^31, two rows: 8 GiB of logits, indices and row offsets past 2^31) -- against the oracle
+    where it can run and otherwise against closed forms that hold bit for bit: 2^31 equal logits
+    sum to exactly 2^31 in any fp32 order (every partial sum is a multiple of the block width below
+    2^31), so every target's logprob is -RN32(ln 2^31); one dominant logit gives -0.0 for itself and
+    the exact shift for the others.  The greedy argmax takes the lowest index among equal maxima."""
+    say("case logprob V=1 and V=257 (block 256)")
+    for V, block in ((1, 256), (257, 256), (4097, 4096)):
+        logits, targets = synth.random_logits(V + 11, 3, V, std=5.0)
+        compare(gpu_logprob(logits, targets, block), oracle.block_logprob(logits, targets, block), f"V={V}")
+        got = host(w8.vocab_argmax(bf16(logits)))
+        assert np.array_equal(got, oracle.argmax(logits)), f"argmax V={V}"
+    V = 1 << 31
+    say(f"case logprob and argmax V=2^31 (two rows, {2 * V * 2 >> 30} GiB)")
+    L = torch.empty((2, V), dtype=torch.bfloat16, device=DEV)
+    L[0].fill_(3.0)
+    L[1].fill_(-150.0)
+    L[1, V - 1] = 2.5
+    tg = torch.tensor([V - 1, V - 1], dtype=torch.int64, device=DEV)
+    out = host(w8.vocab_block_logprob(L, tg, 4096))
+    assert out[0] == -ln_rn32(V), out[0]
+    assert out[1] == 0 and math.copysign(1.0, out[1]) < 0, out[1]
+    out = host(w8.vocab_block_logprob(L, torch.tensor([0, 17], dtype=torch.int64, device=DEV), 4096))
+    assert out[0] == -ln_rn32(V) and out[1] == np.float32(-152.5), out
+    assert list(host(w8.vocab_argmax(L))) == [0, V - 1]
+    L[0, V - 1] = 4.0
+    L[0, V - 2] = 4.0
+    assert list(host(w8.vocab_argmax(L))) == [V - 2, V - 1]
+    del L
+    torch.cuda.empty_cache()
