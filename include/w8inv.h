@@ -92,8 +92,10 @@ const char *w8i_version(void);
  *   t only sets how much padding work is skipped: activation loads whose 8
  *   columns are all padding are not issued (their LDS regions hold zeros),
  *   and the products of such padding columns are not formed (a 32-column
- *   tile with no live column skips its matrix-core steps).  Every live
- *   column's MFMAs, fp64 sums and rounding are the same for every t.
+ *   tile with no live column skips its matrix-core steps); at T_pad 48 or 64
+ *   a call with t <= 32 runs the one-tile kernel of T_pad 32, the second tile
+ *   being padding only.  Every live column's MFMAs, fp64 sums and rounding are
+ *   the same for every t and every T_pad.
  *
  * workspace: this kernel needs none; the size query returns 0 and workspace
  * may be NULL.
@@ -108,8 +110,9 @@ int w8_linear_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_
 /* Name of the kernel that w8_linear_invariant runs for these arguments (static
  * storage; "" for arguments it would reject), for matching profiler records.
  * The choice depends on N, K, T_pad and on whether `scales` is 16-byte
- * aligned -- never on t -- and every kernel runs the K plan above, so it
- * changes no bit of the result.  Pure host function: no device access. */
+ * aligned, and every kernel runs the K plan above, so it changes no bit of the
+ * result.  t enters only at T_pad 48 or 64: a call with t <= 32 runs the kernel
+ * this query names for T_pad 32.  Pure host function: no device access. */
 const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t *scales);
 
 /* ---------------------------------------------------------------------------
@@ -151,8 +154,8 @@ int w8_linear_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint1
                                void *stream);
 
 /* Name of the kernel w8_linear_invariant_packed runs (static storage; "" for
- * arguments it would reject): a function of N and T_pad, never of t.  Pure host
- * function. */
+ * arguments it would reject): a function of N and T_pad (at T_pad 48 or 64 a
+ * call with t <= 32 runs the kernel named for T_pad 32).  Pure host function. */
 const char *w8_linear_invariant_packed_kernel(int64_t N, int64_t K, int32_t T_pad);
 
 /* ---------------------------------------------------------------------------

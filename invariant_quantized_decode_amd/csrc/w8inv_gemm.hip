@@ -39,8 +39,9 @@
 //    offset past the activation buffer's range); a load whose 8 columns are
 //    all padding is not issued at all, its LDS region zeroed once, and the
 //    fp64 products of such columns are not formed (a 32-column tile with no
-//    live column skips its MFMAs).  That is all t selects: how much padding
-//    work is skipped, in groups of 8 columns.
+//    live column skips its MFMAs; at T_pad 48 or 64 with t <= 32 the one-tile
+//    kernel runs, see kernel_width).  That is all t selects: how much padding
+//    work is skipped.
 //  * No atomics; the arithmetic of a column -- K plan, MFMA sequence,
 //    roundings -- depends on neither t, its neighbours, N nor the device.
 #include <hip/hip_runtime.h>
@@ -1074,8 +1075,16 @@ static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S,
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 
+// The width the kernels run at: T_pad, or 32 when T_pad is 48 or 64 and t <= 32.
+// Then the second 32-column tile holds padding columns only, and the one-tile
+// kernels give every live column the same bits: a column's K plan, MFMAs and
+// roundings do not depend on T_pad (nor on which kernel runs it).  Like the
+// skipped activation loads, this only decides how much padding is processed.
+static int kernel_width(int t, int T_pad) { return T_pad > 32 && t <= 32 ? 32 : T_pad; }
+
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                   int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
+    T_pad = kernel_width(t, T_pad);
     const LinearPlan p = plan_linear(N, K, T_pad, S);
     switch (p.kind) {
         case LinearKernel::kTiles:
@@ -1090,6 +1099,7 @@ int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, 
 int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                          int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream) {
     // the persistent kernel where it runs the plain layout, else the split kernel
+    T_pad = kernel_width(t, T_pad);
     if (T_pad <= 32 && tile_count(N) >= kMinTilesPerCu * 256)
         return launch_tiles(Wp, Sp, X, t, T_pad, Y, N, K, ldx, ldy, 2, stream);
     const LinearPlan p = plan_packed(T_pad / 16, (N + kRows - 1) / kRows);
@@ -1100,6 +1110,7 @@ int launch_linear_epilogue(int epi, bool packed, const int8_t* W, const uint16_t
                            int T_pad, uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                            hipStream_t stream) {
     // (SwiGLU: a workgroup covers 16 gate and 16 up rows, one row group of 32)
+    T_pad = kernel_width(t, T_pad);
     const LinearPlan p = packed ? plan_packed(T_pad / 16, epi == kEpiSwiGLU ? (N / 2 + 15) / 16 : (N + kRows - 1) / kRows)
                                 : plan_epilogue(epi, N, K, T_pad, S);
     switch (epi * 2 + (packed ? 1 : 0)) {

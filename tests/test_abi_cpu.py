@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(w8.EXPORTS)
 
 
-def test_kernel_query_never_looks_at_t_and_rejects_bad_shapes():
+def test_kernel_query_is_host_only_and_rejects_bad_shapes():
     """The kernel-name query is host-only; it names one kernel per (N, K, T_pad, scales alignment)."""
     q = L.w8_linear_invariant_kernel
     assert q(6144, 5120, 32, fake(4096)) == b"gemm_w8g32_split_lds<2, 3, true, 0, false>"
