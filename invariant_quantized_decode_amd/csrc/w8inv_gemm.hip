@@ -527,7 +527,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         }
     };
     // one uniform branch per launch: XL = the column groups holding a live
-    // column, rounded up to 1, 2, 4 or all
+    // column, rounded up to 1, 2, 4, 6 (two tiles) or all
     const int live_groups = (t + 7) / 8;
     {
         if (live_groups <= 1) {
@@ -537,6 +537,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         } else if constexpr (kXLoads == 8) {
             if (live_groups <= 4)
                 run(std::integral_constant<int, 4>{});
+            else if (live_groups <= 6)
+                run(std::integral_constant<int, 6>{});
             else
                 run(std::integral_constant<int, 8>{});
         } else {
