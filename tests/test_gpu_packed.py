@@ -103,10 +103,11 @@ def test_packed_persistent_kernel_gives_the_plain_bits(N, K, T_pad):
 @pytest.mark.parametrize("N,K,T_pad", [(1000, 1056, 64), (300, 2080, 32), (70, 544, 16), (131172, 1024, 32)])
 def test_skipped_padding_loads_keep_the_bits(N, K, T_pad):
     """Activation loads whose 8 columns are all padding are not issued, nor are those columns'
-    products formed (a tile with no live column skips its MFMAs); the kernels pick 1, 2, 4 or all
-    column groups per launch.  On both sides of every such boundary (t = 8, 9, 16, 17,
-    32, 33) each column keeps the bits it has at full width, on both layouts and in both kernels
-    (the last case runs the persistent one)."""
+    products formed (a tile with no live column skips its MFMAs, and at T_pad 64 a call with
+    t <= 32 runs the one-tile kernel); the kernels pick 1, 2, 4, 6 (two tiles) or all column groups
+    per launch.  On both sides of every such boundary (t = 8, 9, 16, 17, 32, 33, 48, 49) each column
+    keeps the bits it has at full width, on both layouts and in both kernels (the last case runs
+    the persistent one)."""
     say(f"case padding loads N={N} K={K} T_pad={T_pad}")
     rng = np.random.default_rng(N * 7 + K)
     q = synth.draw_codes(rng, N, K)
@@ -116,7 +117,7 @@ def test_skipped_padding_loads_keep_the_bits(N, K, T_pad):
     Wp, Sp = w8.w8_pack(Wd, Sd)
     full = bits(w8.w8_linear_invariant(Wd, Sd, Xd, T_pad, T_pad))
     assert np.array_equal(bits(w8.w8_linear_invariant_packed(Wp, Sp, Xd, T_pad, T_pad, N)), full)
-    for t in (t for t in (8, 9, 16, 17, 32, 33) if t < T_pad):
+    for t in (t for t in (8, 9, 16, 17, 32, 33, 41, 48, 49) if t < T_pad):
         perm = rng.permutation(T_pad)[:t]
         xp = bf16(x[perm])
         assert np.array_equal(bits(w8.w8_linear_invariant(Wd, Sd, xp, t, T_pad)), full[perm]), t
