@@ -527,22 +527,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         }
     };
     // one uniform branch per launch: XL = the column groups holding a live
-    // column, rounded up to 1, 2, 4, 6 (two tiles) or all
+    // column (two-tile kernels run for t > 32, so theirs start at 4: the first
+    // tile whole)
     const int live_groups = (t + 7) / 8;
-    {
-        if (live_groups <= 1) {
-            run(std::integral_constant<int, 1>{});
-        } else if (live_groups <= 2) {
-            run(std::integral_constant<int, 2>{});
-        } else if constexpr (kXLoads == 8) {
-            if (live_groups <= 4)
-                run(std::integral_constant<int, 4>{});
-            else if (live_groups <= 6)
-                run(std::integral_constant<int, 6>{});
-            else
-                run(std::integral_constant<int, 8>{});
-        } else {
-            run(std::integral_constant<int, kXLoads>{});
+    if constexpr (kXLoads == 4) {
+        switch (live_groups) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
+        }
+    } else {
+        switch (live_groups) {
+            case 5: run(std::integral_constant<int, 5>{}); break;
+            case 6: run(std::integral_constant<int, 6>{}); break;
+            case 7: run(std::integral_constant<int, 7>{}); break;
+            case 8: run(std::integral_constant<int, 8>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
         }
     }
 
@@ -886,13 +887,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         wait_vm<0>();
     };
     if constexpr (PK) {
-        const int live_groups = (t + 7) / 8;
-        if (live_groups <= 1)
-            run(std::integral_constant<int, 1>{});
-        else if (live_groups <= 2)
-            run(std::integral_constant<int, 2>{});
-        else
-            run(std::integral_constant<int, kXLoads>{});
+        switch ((t + 7) / 8) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, kXLoads < 3 ? kXLoads : 3>{}); break;
+            default: run(std::integral_constant<int, kXLoads>{}); break;
+        }
     } else {
         run(std::integral_constant<int, kXLoads>{});
     }

@@ -104,8 +104,8 @@ def test_packed_persistent_kernel_gives_the_plain_bits(N, K, T_pad):
 def test_skipped_padding_loads_keep_the_bits(N, K, T_pad):
     """Activation loads whose 8 columns are all padding are not issued, nor are those columns'
     products formed (a tile with no live column skips its MFMAs, and at T_pad 64 a call with
-    t <= 32 runs the one-tile kernel); the kernels pick 1, 2, 4, 6 (two tiles) or all column groups
-    per launch.  On both sides of every such boundary (t = 8, 9, 16, 17, 32, 33, 48, 49) each column
+    t <= 32 runs the one-tile kernel); the kernels issue the loads of the
+    ceil(t/8) live column groups.  On both sides of every such boundary (t = 8, 9, 16, 17, 32, 33, 48, 49) each column
     keeps the bits it has at full width, on both layouts and in both kernels (the last case runs
     the persistent one)."""
     say(f"case padding loads N={N} K={K} T_pad={T_pad}")
