@@ -16,8 +16,10 @@
  *    and returns W8I_OK.
  *  - Invalid arguments return a negative w8i_status and launch nothing.  No
  *    input is ever silently replaced by another computation.
- *  - The library has no global state and no runtime switches: for given
- *    arguments the arithmetic, and therefore every output bit, is fixed.
+ *  - The library has no runtime switches: for given arguments the
+ *    arithmetic, and therefore every output bit, is fixed.  Its only state is
+ *    the fixed device scratch array of the entry point that allocates nothing
+ *    (vocab_block_logprob_noalloc, at the end of this header).
  */
 #ifndef W8INV_H
 #define W8INV_H
@@ -37,7 +39,8 @@ typedef enum {
     W8I_ET = -4,         /* t < 0, t > T_pad, or T_pad not supported                 */
     W8I_EBLOCK = -5,     /* vocabulary block width not a power of two in [256,32768] */
     W8I_EWORKSPACE = -6, /* workspace NULL or smaller than the size query returns    */
-    W8I_EHIP = -7        /* the HIP runtime reported an error when launching         */
+    W8I_EHIP = -7,       /* the HIP runtime reported an error when launching         */
+    W8I_ESCRATCH = -8    /* the call needs more than the library's fixed scratch     */
 } w8i_status;
 
 /* Human-readable name of a status code (static storage). */
@@ -313,6 +316,36 @@ int w8i_residual_add(const uint16_t *a, const uint16_t *b, uint16_t *y, int32_t 
  * ------------------------------------------------------------------------- */
 int w8i_exp32(const float *x, float *y, int64_t n, void *stream);
 int w8i_log32(const float *x, float *y, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * blockwise target logprob with no workspace argument.
+ *
+ * vocab_block_logprob_noalloc computes exactly what vocab_block_logprob
+ * computes (same kernels, same bits) for the same logits, targets, block,
+ * out, t, V and ldl, with the same argument rules and errors, but its block
+ * maxima and block partials go to a scratch array that the library holds in
+ * device memory: a file-scope device array of W8I_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU the library runs on, kept until the process ends (its
+ * address is looked up on the first call on each device; nothing is
+ * allocated or freed, by this call or any later one).
+ *
+ *   - Calls with vocab_block_logprob_workspace_bytes(t, V, block) larger than
+ *     W8I_NOALLOC_SCRATCH_BYTES return W8I_ESCRATCH and launch nothing
+ *     (1 MiB holds, for example, t = 64 columns of a 248320-entry vocabulary
+ *     in blocks of 256, or t = 32 columns of 2^22 entries in blocks of 4096).
+ *   - Every call on one GPU uses that GPU's one array, and its contents are
+ *     whatever the last call left (every element a call reads is written by
+ *     the same call first).  Calls that can overlap in time on one GPU --
+ *     issued on different streams without ordering between them, or from
+ *     several host threads -- race on the array and give undefined results;
+ *     calls ordered on one stream (or by events) are safe.
+ * ------------------------------------------------------------------------- */
+#define W8I_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+int vocab_block_logprob_noalloc(const uint16_t *logits, const int64_t *targets, int32_t block,
+                                float *out, int32_t t, int64_t V, int64_t ldl, void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libw8inv.so")
 
 W8I_OK = 0
 STATUS = {0: "W8I_OK", -1: "W8I_ENULL", -2: "W8I_ESHAPE", -3: "W8I_EALIGN", -4: "W8I_ET", -5: "W8I_EBLOCK",
-          -6: "W8I_EWORKSPACE", -7: "W8I_EHIP"}
+          -6: "W8I_EWORKSPACE", -7: "W8I_EHIP", -8: "W8I_ESCRATCH"}
 
 EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_bytes", "w8_linear_invariant",
            "w8_linear_invariant_kernel", "w8_linear_add_invariant", "w8_linear_swiglu_invariant",
@@ -30,7 +30,7 @@ EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_by
            "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed",
            "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "vocab_block_logprob_direct",
            "vocab_argmax_workspace_bytes", "vocab_argmax", "w8i_rmsnorm", "w8i_swiglu",
-           "w8i_residual_add", "w8i_exp32", "w8i_log32")
+           "w8i_residual_add", "w8i_exp32", "w8i_log32", "vocab_block_logprob_noalloc")
 
 
 class W8InvError(ValueError):
@@ -66,6 +66,8 @@ def _load():
     L.vocab_block_logprob.restype = ctypes.c_int
     L.vocab_block_logprob_direct.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
     L.vocab_block_logprob_direct.restype = ctypes.c_int
+    L.vocab_block_logprob_noalloc.argtypes = [P, P, I32, P, I32, I64, I64, P]
+    L.vocab_block_logprob_noalloc.restype = ctypes.c_int
     L.vocab_argmax_workspace_bytes.argtypes, L.vocab_argmax_workspace_bytes.restype = [I32, I64], SZ
     L.vocab_argmax.argtypes, L.vocab_argmax.restype = [P, P, I32, I64, I64, P, SZ, P], ctypes.c_int
     L.w8i_rmsnorm.argtypes = [P, P, F32, P, I32, I64, I64, I64, P]
@@ -315,6 +317,32 @@ def vocab_block_logprob(logits: torch.Tensor, targets: torch.Tensor, block: int,
 def vocab_block_logprob_direct(logits: torch.Tensor, targets: torch.Tensor, block: int, **kw) -> torch.Tensor:
     """The blockwise-direct form, target - log(sum_exp): +0.0 for a certain token."""
     return vocab_block_logprob(logits, targets, block, direct=True, **kw)
+
+
+# bytes of the library's fixed device scratch used by vocab_block_logprob_noalloc (W8I_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def vocab_block_logprob_noalloc(logits: torch.Tensor, targets: torch.Tensor, block: int, out: torch.Tensor,
+                                t: int | None = None) -> torch.Tensor:
+    """vocab_block_logprob with no workspace: the library's fixed device scratch holds the block maxima
+    and partials (for callers that cannot allocate; `out` must be given).  Same bits as
+    vocab_block_logprob; calls that overlap in time on one GPU race on the scratch."""
+    if logits.dtype != torch.bfloat16 or logits.dim() != 2:
+        raise ValueError("logits must be a bf16 [t, V] tensor")
+    t = logits.size(0) if t is None else int(t)
+    V = logits.size(1)
+    ldl = _row_major(logits, "logits")
+    if targets.dtype != torch.int64 or targets.numel() < t or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int64 [t] tensor")
+    _dtype(out, "out", torch.float32)
+    if out.numel() < t or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [t] tensor")
+    _same_gpu(("logits", logits), ("targets", targets), ("out", out))
+    st = _launch(_lib.vocab_block_logprob_noalloc, logits.device, _ptr(logits), _ptr(targets), int(block), _ptr(out),
+                 t, V, ldl)
+    _check("vocab_block_logprob_noalloc", st)
+    return out
 
 
 def vocab_argmax_workspace_bytes(t: int, V: int) -> int:

@@ -48,6 +48,7 @@ const char* w8i_status_string(int status) {
         case W8I_EBLOCK: return "W8I_EBLOCK: block width not a power of two in [256, 32768]";
         case W8I_EWORKSPACE: return "W8I_EWORKSPACE: workspace NULL or too small";
         case W8I_EHIP: return "W8I_EHIP: the HIP runtime reported an error";
+        case W8I_ESCRATCH: return "W8I_ESCRATCH: the call needs more than the library's fixed scratch";
         default: return "unknown w8i status";
     }
 }
@@ -173,8 +174,9 @@ size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) 
     return logprob_workspace_bytes(t, V, block);
 }
 
-static int block_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
-                         int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, bool direct, void* stream) {
+// checks shared by the logprob entry points (all but the workspace)
+static int check_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, const float* out, int32_t t,
+                         int64_t V, int64_t ldl) {
     if (block < 256 || block > 32768 || (block & (block - 1)) != 0) return W8I_EBLOCK;
     if (t < 0 || t > 65535) return W8I_ET;
     if (t == 0) return W8I_OK;
@@ -182,6 +184,13 @@ static int block_logprob(const uint16_t* logits, const int64_t* targets, int32_t
     if (V < 1 || V > kMaxDim || ldl < V) return W8I_ESHAPE;
     if ((V + block - 1) / block > 0x7fffffffLL) return W8I_ESHAPE;
     if (!aligned(logits, 2) || !aligned(targets, 8) || !aligned(out, 4)) return W8I_EALIGN;
+    return W8I_OK;
+}
+
+static int block_logprob(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
+                         int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, bool direct, void* stream) {
+    const int st = check_logprob(logits, targets, block, out, t, V, ldl);
+    if (st != W8I_OK || t == 0) return st;
     if (!workspace || workspace_bytes < logprob_workspace_bytes(t, V, block)) return W8I_EWORKSPACE;
     if (!aligned(workspace, 16)) return W8I_EALIGN;
     return launch_logprob(logits, targets, block, out, t, V, ldl, workspace, direct, as_stream(stream));
@@ -195,6 +204,17 @@ int vocab_block_logprob(const uint16_t* logits, const int64_t* targets, int32_t 
 int vocab_block_logprob_direct(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
                                int64_t V, int64_t ldl, void* workspace, size_t workspace_bytes, void* stream) {
     return block_logprob(logits, targets, block, out, t, V, ldl, workspace, workspace_bytes, true, stream);
+}
+
+int vocab_block_logprob_noalloc(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
+                                int64_t V, int64_t ldl, void* stream) {
+    const int st = check_logprob(logits, targets, block, out, t, V, ldl);
+    if (st != W8I_OK || t == 0) return st;
+    if (logprob_workspace_bytes(t, V, block) > W8I_NOALLOC_SCRATCH_BYTES) return W8I_ESCRATCH;
+    void* ws = nullptr;
+    const int sst = noalloc_scratch(&ws);
+    if (sst != W8I_OK) return sst;
+    return launch_logprob(logits, targets, block, out, t, V, ldl, ws, false, as_stream(stream));
 }
 
 size_t vocab_argmax_workspace_bytes(int32_t t, int64_t V) {

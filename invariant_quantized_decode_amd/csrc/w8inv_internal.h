@@ -59,6 +59,9 @@ const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad);
 size_t logprob_workspace_bytes(int t, int64_t V, int block);
 int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,
                    int64_t ldl, void* ws, bool direct, hipStream_t stream);
+// device address of the current device's fixed scratch array (W8I_NOALLOC_SCRATCH_BYTES bytes),
+// looked up once per device; allocates nothing
+int noalloc_scratch(void** ptr);
 
 constexpr int kArgmaxBlock = 4096;  // vocabulary entries per workgroup of the argmax's first pass
 size_t argmax_workspace_bytes(int t, int64_t V);

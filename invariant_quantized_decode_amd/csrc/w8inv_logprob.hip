@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "w8inv_internal.h"
 #include "w8inv_math.h"
 
@@ -283,6 +285,34 @@ int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* 
     else
         hipLaunchKernelGGL(lp_fold<false>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
     return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+}
+
+// ------------------------------------------- scratch of the no-alloc entry point
+// vocab_block_logprob_noalloc keeps its block maxima and partials here instead
+// of in a caller's workspace.  Every GPU the library runs on holds its own copy
+// of this array, at its own address, until the process ends.  In host code the
+// array's name is not a device address: it is looked up once per device with
+// hipGetSymbolAddress (that device current), and only that address is ever
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[W8I_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+int noalloc_scratch(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return W8I_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W8I_EHIP;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return W8I_OK;
 }
 
 // ------------------------------------------------------- verification hooks

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -43,7 +43,7 @@ def test_kernel_query_is_host_only_and_rejects_bad_shapes():
 
 def test_status_strings_and_version():
     assert L.w8i_status_string(0) == b"W8I_OK"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         assert L.w8i_status_string(code).decode().startswith(w8.STATUS[code])
     assert b"gfx950" in L.w8i_version()
 
@@ -180,6 +180,24 @@ def test_logprob_workspace_size():
     assert need >= 2 * 32 * nb * 4 and need % 256 == 0
     assert L.vocab_block_logprob_workspace_bytes(32, 248320, 1000) == 0
     assert logprob(t=0, Lg=0, T=0, out=0, ws=0) == 0
+
+
+def test_noalloc_logprob_validation():
+    """The entry point that allocates nothing validates like vocab_block_logprob and refuses, before any
+    device access, a call whose maxima and partials would not fit the fixed 1 MiB scratch."""
+    f = L.vocab_block_logprob_noalloc
+    assert w8.NOALLOC_SCRATCH_BYTES == 1 << 20
+    assert f(fake(A), fake(A), 1000, fake(A), 4, 248320, 248320, None) == -5
+    assert f(fake(A), fake(A), 4096, fake(A), -1, 248320, 248320, None) == -4
+    assert f(None, None, 4096, None, 0, 248320, 248320, None) == 0
+    assert f(None, fake(A), 4096, fake(A), 4, 248320, 248320, None) == -1
+    assert f(fake(A), fake(A), 4096, fake(A), 4, 248320, 1000, None) == -2
+    assert f(fake(A), fake(A + 4), 4096, fake(A), 4, 248320, 248320, None) == -3
+    # 64 columns x 2^22 entries in blocks of 4096: 2 x 256 KiB fits; blocks of 256: 2 x 4 MiB does not
+    assert L.vocab_block_logprob_workspace_bytes(64, 1 << 22, 4096) <= 1 << 20
+    assert L.vocab_block_logprob_workspace_bytes(64, 1 << 22, 256) > 1 << 20
+    assert f(fake(A), fake(A), 256, fake(A), 64, 1 << 22, 1 << 22, None) == -8
+    assert L.w8i_status_string(-8).decode().startswith("W8I_ESCRATCH")
 
 
 def test_glue_and_hooks_reject_invalid_arguments():
