@@ -56,6 +56,7 @@ def lib():
         L.oracle_exp32_array.argtypes = [P, I64, P]
         L.oracle_log32_array.argtypes = [P, I64, P]
         L.oracle_exp32_bits.argtypes = [U32, I64, P]
+        L.oracle_log32_bits.argtypes = [U32, I64, P]
         L.oracle_bf16_round.argtypes, L.oracle_bf16_round.restype = [F64], ctypes.c_uint16
         L.oracle_bf16_value.argtypes, L.oracle_bf16_value.restype = [ctypes.c_uint16], F64
         L.oracle_f16_value.argtypes, L.oracle_f16_value.restype = [ctypes.c_uint16], F64
@@ -155,6 +156,12 @@ def log32(x) -> np.ndarray:
 def exp32_bits(start: int, count: int) -> np.ndarray:
     out = np.empty(count, dtype=np.float32)
     lib().oracle_exp32_bits(start, count, _ptr(out))
+    return out
+
+
+def log32_bits(start: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.float32)
+    lib().oracle_log32_bits(start, count, _ptr(out))
     return out
 
 

@@ -160,6 +160,17 @@ void oracle_exp32_bits(uint32_t start, int64_t count, float *out) {
     }
 }
 
+/* LOG32 of the `count` consecutive binary32 bit patterns starting at `start`. */
+void oracle_log32_bits(uint32_t start, int64_t count, float *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t u = start + (uint32_t)i;
+        float x;
+        memcpy(&x, &u, sizeof x);
+        out[i] = oracle_log32(x);
+    }
+}
+
 /* ------------------------------------------------------ block logprob */
 
 /* Balanced pairwise tree over w (a power of two) values in index order:

@@ -136,6 +136,29 @@ def test_in_block_tree_is_pairwise_not_sequential():
     assert part2[0, 0] == part[0, 0]
 
 
+def test_in_block_tree_pairs_neighbours_not_strided_halves():
+    """A 256-wide block with the row max at indices 0 and 128 (e = 1 each), d = EXP32(-15.75) at index 1
+    and every other entry far below the max (e = +0).  d lies strictly between 2^-23 and 1.5 * 2^-23
+    (checked against a decimal exp), which fixes every rounding:
+      * index-order pairwise tree: T(0,2) = RN(1 + d) = 1 + 2^-23 and zeros keep it up to T(0,128);
+        T(128,128) = 1; P = RN(2 + 2^-23) = 2, a tie resolved to even;
+      * strided pairing (i with i + 128, then i with i + 64, ...): 1 + 1 = 2 first, and d joins last:
+        RN(2 + d) = 2 + 2^-22.
+    So the partial is exactly 2 and the logprob of the target at index 0 is -RN32(ln 2); the strided
+    tree would give -RN32(ln(2 + 2^-22)), two ulps away."""
+    block = 256
+    d = exp_rn32(-15.75)
+    assert 2.0 ** -23 < float(d) < 1.5 * 2.0 ** -23
+    assert float(np.float32(2.0) + d) == 2.0 + 2.0 ** -22      # the strided order's last add
+    row = np.full(block, bf16(-200.0), dtype=np.uint16)
+    row[0] = row[128] = bf16(0.0)
+    row[1] = bf16(-15.75)
+    out, part = oracle.block_logprob(row[None], np.array([0], dtype=np.int64), block, return_partials=True)
+    assert part[0, 0] == 2.0
+    assert out[0] == -ln_rn32(2.0)
+    assert ln_rn32(2.0) != ln_rn32(2.0 + 2.0 ** -22)
+
+
 def test_virtual_padding_equals_materialised_minus_inf():
     rng = np.random.default_rng(4)
     V, block = 3 * 256 + 17, 256

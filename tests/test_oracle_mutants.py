@@ -33,6 +33,11 @@ MUTANTS = {
     "sequential in-block sum": (
         "    if (w == 1) return e[0];\n    float left",
         "    if (w >= 1) { float a = e[0]; for (int64_t i = 1; i < w; ++i) a += e[i]; return a; }\n    float left"),
+    "strided in-block tree": (
+        "    if (w == 1) return e[0];\n    float left",
+        "    if (w > 1) { float *a = (float *)malloc((size_t)w * sizeof(float)); memcpy(a, e, (size_t)w * sizeof(float));"
+        " for (int64_t h = w / 2; h >= 1; h /= 2) for (int64_t i = 0; i < h; ++i) a[i] = a[i] + a[i + h];"
+        " float r = a[0]; free(a); return r; }\n    if (w == 1) return e[0];\n    float left"),
     "per-block max shift": (
         "float shifted = bf16_as_float(l[v]) - m;",
         "float bm = -INFINITY; for (int64_t u = (v / block) * block; u < (v / block + 1) * block && u < V; ++u) {"
