@@ -47,7 +47,7 @@ def lib():
         L = ctypes.CDLL(path)
         P, I64, U32, F32, F64, I32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
                                       ctypes.c_float, ctypes.c_double, ctypes.c_int)
-        L.oracle_w8_linear.argtypes = [P, P, P, I64, I64, I64, I64, P, I64, P]
+        L.oracle_w8_linear.argtypes = [P, P, P, I64, I64, I64, I64, P, I64, P, P]
         L.oracle_block_logprob.argtypes = [P, P, I64, I64, I64, I64, P, P, I32]
         L.oracle_argmax.argtypes = [P, I64, I64, I64, P]
         L.oracle_logprob_ref.argtypes = [P, P, I64, I64, I64, P]
@@ -80,8 +80,10 @@ def max_threads() -> int:
     return int(lib().oracle_max_threads())
 
 
-def w8_linear(q, s, x, rows=None) -> np.ndarray:
-    """fp64 y[t, len(rows)] = dequant(W)[rows] . x^T  (x is [t, K] bf16 bits)."""
+def w8_linear(q, s, x, rows=None, mass: bool = False):
+    """fp64 y[t, len(rows)] = dequant(W)[rows] . x^T  (x is [t, K] bf16 bits).
+
+    mass=True returns (y, m) with m the absolute sums sum_k |q s x| of the same terms."""
     q = _c(q, np.int8)
     s = _c(s, np.uint16)
     x = _c(x, np.uint16)
@@ -95,9 +97,11 @@ def w8_linear(q, s, x, rows=None) -> np.ndarray:
         assert rows.min(initial=0) >= 0 and rows.max(initial=0) < N
         nrows, rp = rows.size, _ptr(rows)
     y = np.empty((t, nrows), dtype=np.float64)
+    m = np.empty((t, nrows), dtype=np.float64) if mass else None
     if t and nrows:
-        lib().oracle_w8_linear(_ptr(q), _ptr(s), _ptr(x), N, K, t, K, rp, nrows, _ptr(y))
-    return y
+        lib().oracle_w8_linear(_ptr(q), _ptr(s), _ptr(x), N, K, t, K, rp, nrows, _ptr(y),
+                               _ptr(m) if mass else None)
+    return (y, m) if mass else y
 
 
 def block_logprob(logits, targets, block: int, return_partials: bool = False, direct: bool = False):

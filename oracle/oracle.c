@@ -104,10 +104,14 @@ int oracle_max_threads(void) { return omp_get_max_threads(); }
  *   s : fp16  [N, K/32] row-major, one scale per row and 32 consecutive k
  *   x : bf16  [t, ldx] row-major (column j of the activations is row j here)
  * Each row's weights are dequantised once into fp64 (exact), then each column
- * is a plain fp64 dot product in ascending k. */
+ * is a plain fp64 dot product in ascending k.
+ * When mass != NULL it also receives the absolute sum of the same terms,
+ * mass[j * nrows + i] = sum_k |q[n, k] * s[n, k / 32] * x[j, k]|: the scale
+ * below which an fp32 accumulation of these terms cannot resolve the result
+ * (one fp32 ulp of a partial sum of that size). */
 void oracle_w8_linear(const int8_t *q, const uint16_t *s, const uint16_t *x,
                       int64_t N, int64_t K, int64_t t, int64_t ldx,
-                      const int64_t *rows, int64_t nrows, double *y) {
+                      const int64_t *rows, int64_t nrows, double *y, double *mass) {
     const int64_t G = K / 32;
     (void)N;
 #pragma omp parallel
@@ -126,6 +130,12 @@ void oracle_w8_linear(const int8_t *q, const uint16_t *s, const uint16_t *x,
                 for (int64_t k = 0; k < K; ++k)
                     acc += w[k] * (double)bf16_as_float(xr[k]);
                 y[j * nrows + i] = acc;
+                if (mass) {
+                    double a = 0.0;
+                    for (int64_t k = 0; k < K; ++k)
+                        a += fabs(w[k] * (double)bf16_as_float(xr[k]));
+                    mass[j * nrows + i] = a;
+                }
             }
         }
         free(w);

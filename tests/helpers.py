@@ -39,6 +39,24 @@ def within_bf16_ulps(y_bits, y_ref, n_ulps=2.0):
     return err <= n_ulps, err
 
 
+FP32_FLOOR = 2.0 ** -24  # one fp32 rounding, relative
+
+
+def parity_bar(y_bits, y_ref, mass, n_ulps=2.0):
+    """The projection's per-element bar: |y - y_ref| <= n_ulps * ulp_bf16(y_ref), except where the exact
+    value has cancelled below what an fp32 accumulation of the terms can resolve -- then |y - y_ref|
+    must lie within one fp32 rounding of the terms' absolute sum, 2^-24 * sum_k |q s x| (`mass`).
+    Returns (ok_mask, err_in_ulps, misses): misses = the outputs beyond n_ulps ulps that pass only by
+    that floor (reported per workload)."""
+    y = bf16_bits_to_f64(y_bits)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    d = np.abs(y - y_ref)
+    err = d / ulp_bf16(y_ref)
+    in_ulps = err <= n_ulps
+    ok = in_ulps | (d <= FP32_FLOOR * np.asarray(mass, dtype=np.float64))
+    return ok, err, int(np.sum(ok & ~in_ulps))
+
+
 def rn32(x) -> np.float32:
     """Correctly round an exact value (Fraction, Decimal, int or float) to binary32, ties to even."""
     f = Fraction(x)

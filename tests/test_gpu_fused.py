@@ -103,18 +103,19 @@ def test_linear_swiglu_equals_linear_then_swiglu(F, K, t, T_pad, aligned):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("T_pad", [32, 64])
+@pytest.mark.parametrize("T_pad", [16, 32, 48, 64])
 def test_fused_columns_are_t_invariant(T_pad):
     """A column's bits do not depend on t or on the other columns (the pages' fixed-width contract),
-    on both layouts; at T_pad 64 the t <= 32 cases leave the second 32-column tile without a live
-    column (its products are skipped)."""
+    on both layouts; at T_pad 48 and 64 the t <= 32 cases run the one-tile kernel (the second
+    32-column tile would hold no live column), and the t values reach every count of live 8-column
+    groups (1..8) the epilogue kernels have a loop copy for."""
     rng, q, s, x = draw(9 + T_pad, 2 * 96, 1024, T_pad)
     res = synth.draw_acts(rng, T_pad, 2 * 96)
     Wd, Sd, Xd, Rd = i8(q), f16(s), bf16(x), bf16(res)
     Wp, Sp = w8.w8_pack(Wd, Sd)
     full_sw = bits(w8.w8_linear_swiglu_invariant(Wd, Sd, Xd, T_pad, T_pad))
     full_add = bits(w8.w8_linear_add_invariant(Wd, Sd, Xd, Rd, T_pad, T_pad))
-    for t in (t for t in (1, 5, 9, 17, 31, 33, 63) if t < T_pad):
+    for t in (t for t in (1, 5, 9, 17, 31, 33, 41, 49, 63) if t < T_pad):
         perm = rng.permutation(T_pad)[:t]
         say(f"case fused T_pad={T_pad} t={t}")
         xp, rp = bf16(x[perm]), bf16(res[perm])

@@ -100,14 +100,17 @@ def test_packed_persistent_kernel_gives_the_plain_bits(N, K, T_pad):
         assert np.array_equal(bits(w8.w8_linear_invariant_packed(Wp, Sp, Xd, t, T_pad, N)), plain)
 
 
-@pytest.mark.parametrize("N,K,T_pad", [(1000, 1056, 64), (300, 2080, 32), (70, 544, 16), (131172, 1024, 32)])
+@pytest.mark.parametrize("N,K,T_pad", [(1000, 1056, 64), (300, 2080, 32), (70, 544, 16), (131172, 1024, 32),
+                                       (257, 1056, 48), (131172, 1056, 64)])
 def test_skipped_padding_loads_keep_the_bits(N, K, T_pad):
     """Activation loads whose 8 columns are all padding are not issued, nor are those columns'
-    products formed (a tile with no live column skips its MFMAs, and at T_pad 64 a call with
-    t <= 32 runs the one-tile kernel); the kernels issue the loads of the
-    ceil(t/8) live column groups.  On both sides of every such boundary (t = 8, 9, 16, 17, 32, 33, 48, 49) each column
-    keeps the bits it has at full width, on both layouts and in both kernels (the last case runs
-    the persistent one)."""
+    products formed (a tile with no live column skips its MFMAs, and at T_pad 48 or 64 a call with
+    t <= 32 runs the one-tile kernel of T_pad 32); the kernels issue the loads of the
+    ceil(t/8) live column groups.  On both sides of every such boundary (t = 8, 9, 16, 17, 32, 33,
+    41, 48, 49) each column keeps the bits it has at full width, on both layouts.  The fourth case
+    runs the persistent kernel throughout; in the last one (odd K/32, scales per stage) the kernel
+    family itself changes at t = 32 / 33: the persistent one-tile kernel up to 32 columns, the
+    two-tile split kernel above."""
     say(f"case padding loads N={N} K={K} T_pad={T_pad}")
     rng = np.random.default_rng(N * 7 + K)
     q = synth.draw_codes(rng, N, K)

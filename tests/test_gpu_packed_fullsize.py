@@ -3,7 +3,8 @@ benchmark times: weights packed once by w8_pack, calls captured in a HIP graph a
 
 For each workload (1024x5120 T_pad 16, 6144x5120 T_pad 32, gate/up 34816x5120 and down
 5120x17408 T_pad 64, the 248320x5120 head T_pad 32) and t in {1, T_pad}:
-  * sampled rows are within 2 bf16 ulps of the fp64 oracle (computed row by row);
+  * every output is within 2 bf16 ulps of the fp64 oracle, or -- where the exact value has cancelled
+    below what fp32 accumulation can resolve -- within one fp32 rounding of sum |q s x| (counted);
   * every graph replay gives the eager call's bits, with eager work and synchronisation between
     the replays;
   * columns of a permuted subset keep their full-width bits (t-invariance on this path).
@@ -14,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import within_bf16_ulps
+from tests.helpers import parity_bar, within_bf16_ulps
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -44,14 +45,14 @@ def check(label, q, s, x, T_pad, rng):
     Xd = bf16(x)
     kernel = w8.w8_linear_invariant_packed_kernel(N, K, T_pad)
     full = None
+    ref, mass = oracle.w8_linear(q, s, x, mass=True)  # x[:t] is a prefix of x: rows [:t] are the oracle at t
     for t in (T_pad, 1):
         say(f"case packed full size {label} t={t} ({kernel})")
         eager = w8.w8_linear_invariant_packed(Wp, Sp, Xd[:t], t, T_pad, N)
         want = bits(eager)
-        rows = np.sort(np.concatenate([rng.choice(N, size=384, replace=False), [0, N - 1]]))
-        ok, err = within_bf16_ulps(want[:, rows], oracle.w8_linear(q, s, x[:t], rows=rows), 2.0)
-        say(f"{label} t={t}: max err {float(err.max()):.3f} ulp over {ok.size} sampled outputs")
-        assert ok.all(), f"{label} t={t}: {int((~ok).sum())} sampled outputs beyond 2 ulps"
+        ok, err, misses = parity_bar(want, ref[:t], mass[:t])
+        say(f"{label} t={t}: all {ok.size} outputs, {misses} beyond 2 ulps within the fp32 floor")
+        assert ok.all(), f"{label} t={t}: {int((~ok).sum())} outputs outside the parity bar"
         if full is None:
             full = want
         else:

@@ -194,3 +194,26 @@ def test_mistakes_are_detected_by_the_pins():
     wrong = np.array([[oracle.f16_value(int(s[n, 2])) * xv[j, 32:64].sum() for n in range(N)] for j in range(t)])
     assert np.allclose(y, right, rtol=1e-12)
     assert not np.allclose(y, wrong, rtol=1e-6)
+
+
+def test_absolute_mass_is_the_sum_of_absolute_terms():
+    """The oracle's second output, sum_k |q s x| (the fp32 accumulation floor's scale): for all-ones
+    weights with unit scales and x on a 1/16 grid it is the exact sum of |x| (math.fsum); for random
+    signed codes and activations it equals, bit for bit, the plain projection of |q| and |x| (every term
+    is the same exact fp64 product, summed in the same order); it is never below |y|."""
+    K, t = 5120, 6
+    rng = np.random.default_rng(21)
+    xi = rng.integers(-64, 65, size=(t, K)).astype(np.float32) / 16
+    x = synth.f32_to_bf16_bits(xi)
+    q1 = np.ones((8, K), dtype=np.int8)
+    s1 = np.full((8, K // 32), F16_ONE, dtype=np.uint16)
+    _, m1 = oracle.w8_linear(q1, s1, x, mass=True)
+    for j in range(t):
+        assert np.all(m1[j] == math.fsum(abs(float(v)) for v in xi[j]))
+    q, s, x2 = synth.small_linear(22, 64, 1024, 5, 0.0)
+    y, m = oracle.w8_linear(q, s, x2, mass=True)
+    y_abs = oracle.w8_linear(np.abs(q.astype(np.int16)).astype(np.int8), s, x2 & np.uint16(0x7FFF))
+    assert np.array_equal(m, y_abs)
+    assert np.all(m >= np.abs(y))
+    assert np.array_equal(oracle.w8_linear(q, s, x2), y)
+

@@ -24,6 +24,8 @@ MUTANTS = {
     "neighbouring column mixed in": (
         "acc += w[k] * (double)bf16_as_float(xr[k]);",
         "acc += w[k] * (double)bf16_as_float((xr + (j ^ 1 < t ? (j ^ 1) - j : 0) * ldx)[k]);"),
+    "absolute mass keeps the signs": (
+        "a += fabs(w[k] * (double)bf16_as_float(xr[k]));", "a += w[k] * (double)bf16_as_float(xr[k]);"),
     "fp16 subnormal scales flushed": ("v = ldexp((double)m, -24);", "v = 0.0;"),
     "fp32 instead of fp64 accumulation": ("double acc = 0.0;", "float acc = 0.0f;"),
     "block fold reversed": (
