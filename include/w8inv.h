@@ -55,10 +55,11 @@ const char *w8i_version(void);
  * Source: the ninfer issue on t-dependent kernel dispatch (GitHub issue 80),
  * table "Where t selects arithmetic" row "ops::linear W8G32" (int8 weights,
  * one scale per 32 consecutive K elements, 16-bit activations) and the
- * "Proposal: opt-in fixed decode width" section: every call runs one kernel
- * schedule at the padded width T_pad, padded columns are never read from the
- * caller and never stored, columns never mix, so column j's bits do not
- * depend on t, on j's neighbours or on the order of the columns.
+ * "Proposal: opt-in fixed decode width" section: one reduction schedule, set
+ * by the padded width T_pad, serves every real t; padding columns are never
+ * read from the caller nor stored, and no output column's arithmetic involves
+ * another column, so column j's bits depend neither on t, on j's neighbours
+ * nor on the order of the columns.
  *
  *   y[j, n] = bf16_rne( sum_k  q[n, k] * s[n, k / 32] * x[j, k] )   j < t, n < N
  *

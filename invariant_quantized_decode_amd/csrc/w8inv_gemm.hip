@@ -3,10 +3,10 @@
 // every t.
 //
 // Method: the ninfer issue on t-dependent kernel dispatch (GitHub issue 80),
-// "Proposal: opt-in fixed decode width" -- the kernel and its internal
-// schedule are the same for every real t <= T_pad, padded columns are zero
-// and ignored, columns never mix.  Format: table "Where t selects
-// arithmetic", row "ops::linear W8G32".
+// "Proposal: opt-in fixed decode width": one reduction schedule serves every
+// t <= T_pad, padding columns are never read from the caller nor stored, and
+// no output column's arithmetic involves another column.  Format: table
+// "Where t selects arithmetic", row "ops::linear W8G32".
 //
 // Design for gfx950 (CDNA4):
 //  * The K plan is a function of K alone: 8 contiguous K-slices made of whole

@@ -12,7 +12,8 @@
  *  - ninfer issue "t-dependent kernel dispatch" (GitHub issue 80), table
  *    "Where t selects arithmetic", row "ops::linear W8G32": int8 weights with
  *    one scale per 32 consecutive K elements and 16-bit activations; the
- *    "Proposal" section: columns never mix, so y[:, j] = dequant(W) x[:, j]
+ *    "Proposal" section: each output column depends on its own activation
+ *    column only, so y[:, j] = dequant(W) x[:, j]
  *    is a per-column result.  The oracle is that definition written out:
  *    every term q * s * x is exact in fp64 (7 + 11 + 8 significant bits) and
  *    the terms are summed in fp64 in ascending k.

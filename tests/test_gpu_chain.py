@@ -7,11 +7,12 @@ attention, which is outside this library) -> O 5120x6144 -> + residual -> RMSNor
 
 32 lanes of hidden state run 200 steps; each step takes t random distinct lanes (t uniform in
 1..32) in random slot order.  The invariance pin (the ninfer issue's "Proposal: opt-in fixed
-decode width": one schedule at the padded width, columns never mix): every lane replayed alone
-(t = 1, slot 0) reproduces bit for bit every state it had inside the compositions.  The values
-are checked against the oracle on the chain's own inputs at two steps (the first, with N(0, 1)
-states, and a late one, where the residual stream has grown to ~1e7): every output of each
-projection within 2 bf16 ulps, each glue op within 1 bf16 ulp.
+decode width": one schedule at the padded width, no column's arithmetic touching another's):
+every lane replayed alone (t = 1, slot 0) reproduces bit for bit every state it had inside the
+compositions.  The values are checked against the oracle on the chain's own inputs at two steps
+(the first, with N(0, 1) states, and a late one, where the residual stream has grown to ~1e7):
+every output of each projection within the parity bar (2 bf16 ulps; the fp32 accumulation floor
+where the exact value cancels), each glue op within 1 bf16 ulp.
 """
 import numpy as np
 import pytest

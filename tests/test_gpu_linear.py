@@ -5,7 +5,7 @@ tolerance; the ninfer page, "Reading" paragraph under "Measured", puts
 schedule-to-schedule differences at 1-2 bf16 ulps).  Invariance: every column's
 bits are identical for every t <= T_pad, under column permutations, across
 repeats, across T_pad and across row slices (the page's "Proposal: opt-in
-fixed decode width": columns never mix, one schedule for every t).
+fixed decode width": no column's arithmetic involves another, one schedule for every t).
 """
 import numpy as np
 import pytest
