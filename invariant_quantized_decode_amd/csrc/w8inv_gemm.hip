@@ -152,6 +152,11 @@ __device__ __forceinline__ constexpr int tile_live_values(int tt, int xl, int nv
 // no memory is read; the stage and piece offsets added to it stay below 2^32.
 constexpr uint32_t kPadColumnOffset = 0x80000000u;
 
+// Scheduling-barrier mask that lets every instruction class except the vector
+// memory ones move across the barrier (ALU, VALU, SALU, MFMA, LDS, transcendental):
+// the loads keep the issue order the explicit waits count on.
+constexpr int kKeepVmemOrder = 0x078F;
+
 // s_waitcnt that waits until at most N vector-memory operations are pending
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -346,6 +351,56 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         }
     };
 
+    // Both groups of a full stage at once, ordered for latency as in the
+    // persistent kernel: the A operands are read from LDS first, the two
+    // groups' MFMA chains are interleaved, group 0's fp64 epilogue runs under
+    // group 1's.  Per output the operations and their order are those of
+    // step(0) then step(1).
+    auto step2 = [&](auto XLc, const u32x4 (&w)[2], const uint16_t (&ss)[2], uint32_t sp, const unsigned char* xs,
+                     int g) {
+        constexpr int XL = decltype(XLc)::value;
+        u32x4 a[2][NT][2];
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                if (tile_live_values(tt, XL, (tt == NT - 1) ? kLastValues : 16) == 0) continue;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) a[gs][tt][h] = *reinterpret_cast<const u32x4*>(xs + xa_off[tt][gs][h]);
+            }
+        bf16x8 b_lo[2], b_hi[2];
+        double sc[2];
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs) {
+            b_lo[gs] = dequant8(w[gs].x, w[gs].y);
+            b_hi[gs] = dequant8(w[gs].z, w[gs].w);
+            const uint16_t s16 = PK ? (uint16_t)(sp >> (16 * gs)) : LS ? s_lds[s_row_lds + g + gs] : ss[gs];
+            sc[gs] = (double)(float)__builtin_bit_cast(_Float16, s16);
+        }
+        f32x16 d[2][NT];
+        const f32x16 zero = {};
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            if (tile_live_values(tt, XL, (tt == NT - 1) ? kLastValues : 16) == 0) continue;
+#pragma unroll
+            for (int gs = 0; gs < 2; ++gs)
+                d[gs][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[gs][tt][0]), b_lo[gs],
+                                                                    zero, 0, 0, 0);
+#pragma unroll
+            for (int gs = 0; gs < 2; ++gs)
+                d[gs][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[gs][tt][1]), b_hi[gs],
+                                                                    d[gs][tt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int nv = tile_live_values(tt, XL, (tt == NT - 1) ? kLastValues : 16);
+#pragma unroll
+                for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(sc[gs], (double)d[gs][tt][v], acc[tt][v]);
+            }
+    };
+
     // The stages' loads, for XL = XLc direct activation loads per stage.  A
     // direct load covers 8 columns; those whose 8 columns are all padding
     // (j >= t) are not issued, and their LDS regions are zeroed once here, so
@@ -394,8 +449,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
         auto compute = [&](auto U) {
             constexpr int u = decltype(U)::value;
             if constexpr (!PK) swap16(ring[u][0], ring[u][1]);
-            step(XLc, ring[u], sring[u], pring[u], slot(u), 0, g);
-            step(XLc, ring[u], sring[u], pring[u], slot(u), 1, g + 1);
+            step2(XLc, ring[u], sring[u], pring[u], slot(u), g);
         };
         // Only real stages are loaded: the first min(D, full) up front, then
         // stage q + D right after stage q is computed, while q + D < full.
@@ -753,6 +807,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // the running total as soon as the groups before the next stage are done
     // (empty slices, possible when K < 512, fold a +0 sum like any other).
     int slice = 0;
+    int next_bound = (int)kslice_begin(G, 1);  // first group of slice `slice + 1`
     auto fold_slice = [&]() {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
@@ -762,6 +817,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                 acc[tt][v] = 0.0;
             }
         ++slice;
+        next_bound = (int)kslice_begin(G, slice + 1);
     };
 
     // The loop, for XL = XLc direct activation loads per wave per block.  With
@@ -818,50 +874,102 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             __builtin_amdgcn_sched_barrier(0);
             const bool live = b < nb;
             const int g0 = block_g(b);
+            // A one-stage software pipeline.  fetch(u) reads stage u's matrix-core
+            // A operands from LDS (the block's activations are all there since the
+            // barrier), dequantises its weights from the register ring and decodes
+            // its two scales; stage u's MFMAs are issued, its ring slot is reloaded
+            // with the next block's stage u, stage u + 1 is fetched under those
+            // MFMAs, and only then does stage u's fp64 epilogue run.  Per output the
+            // operations and their order are unchanged: group g's two MFMAs from
+            // zero, then acc = fma(s_g, D_g, acc) for g and then for g + 1 (odd G:
+            // the tile's last stage has one group; its second chain runs on the
+            // zero or repeated group the loads bring and is not accumulated).
+            struct StageOps {
+                u32x4 a[2][NT][2];
+                bf16x8 lo[2], hi[2];
+                double s[2];
+            };
+            auto fetch = [&](int u, StageOps& o) {
+                WStage& cur = ring[u];
+                if constexpr (!PK) swap16(cur.w[0], cur.w[1]);
+#pragma unroll
+                for (int gs = 0; gs < 2; ++gs)
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        if (tile_live_values(tt, XG, 16) == 0) continue;
+                        const unsigned char* xt = xs + u * kStageBytes + tt * kXTileBytes;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            o.a[gs][tt][h] = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c + h));
+                    }
+#pragma unroll
+                for (int gs = 0; gs < 2; ++gs) {
+                    o.lo[gs] = dequant8(cur.w[gs].x, cur.w[gs].y);
+                    o.hi[gs] = dequant8(cur.w[gs].z, cur.w[gs].w);
+                    uint16_t s16;
+                    if constexpr (SC)
+                        s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
+                    else if constexpr (PK)
+                        s16 = (uint16_t)(cur.sp >> (16 * gs));
+                    else
+                        s16 = cur.s[gs];
+                    o.s[gs] = (double)(float)__builtin_bit_cast(_Float16, s16);
+                }
+            };
+            StageOps ops[2];
+            // stage 0's loads have landed once only the loads issued after them
+            // are pending: the block's other stages, the next block's activations
+            // (and scales)
+            wait_vm<(kBlockStages - 1) * LW + XL + LS>();
+            fetch(0, ops[0]);
 #pragma unroll
             for (int u = 0; u < kBlockStages; ++u) {
-                // stage u's loads have landed once only the loads issued after
-                // them are pending (the same count for every stage)
-                wait_vm<(kBlockStages - 1) * LW + XL + LS>();
-                WStage& cur = ring[u];
+                StageOps& o = ops[u & 1];
                 const int g = g0 + 2 * u;
-                if (live && g < G) {
-                    if constexpr (!PK) swap16(cur.w[0], cur.w[1]);
-                    while (kslice_begin(G, slice + 1) <= g) fold_slice();
-                    const int ng = (g + 1 < G) ? 2 : 1;
+                const bool work = live && g < G;
+                f32x16 d[2][NT];
+                if (work) {
+                    while (next_bound <= g) fold_slice();
+                    const f32x16 zero = {};
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        if (tile_live_values(tt, XG, 16) == 0) continue;
+#pragma unroll
+                        for (int gs = 0; gs < 2; ++gs)
+                            d[gs][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8, o.a[gs][tt][0]), o.lo[gs], zero, 0, 0, 0);
+#pragma unroll
+                        for (int gs = 0; gs < 2; ++gs)
+                            d[gs][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8, o.a[gs][tt][1]), o.hi[gs], d[gs][tt], 0, 0, 0);
+                    }
+                }
+                // the loads keep their issue order (the waits count on it); other
+                // work may move across
+                __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+                load_stage(b + 1, u, ring[u]);
+                __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+                if (u + 1 < kBlockStages) {
+                    // stage u + 1's loads: after them are pending the block's later
+                    // stages, the next block's activations (and scales) and its
+                    // stages 0..u -- the same count as for stage 0
+                    wait_vm<(kBlockStages - 1) * LW + XL + LS>();
+                    fetch(u + 1, ops[(u + 1) & 1]);
+                }
+                if (work) {
+                    const int ngs = g + 1 < G ? 2 : 1;
 #pragma unroll
                     for (int gs = 0; gs < 2; ++gs) {
-                        if (gs >= ng) break;  // odd G: the tile's last stage has one group
-                        const bf16x8 b_lo = dequant8(cur.w[gs].x, cur.w[gs].y);
-                        const bf16x8 b_hi = dequant8(cur.w[gs].z, cur.w[gs].w);
-                        uint16_t s16;
-                        if constexpr (SC)
-                            s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
-                        else if constexpr (PK)
-                            s16 = (uint16_t)(cur.sp >> (16 * gs));
-                        else
-                            s16 = cur.s[gs];
-                        const double scale = (double)(float)__builtin_bit_cast(_Float16, s16);
+                        if (gs >= ngs) break;
 #pragma unroll
                         for (int tt = 0; tt < NT; ++tt) {
                             const int nv = tile_live_values(tt, XG, (tt == NT - 1) ? kLastValues : 16);
-                            if (nv == 0) continue;
-                            const unsigned char* xt = xs + u * kStageBytes + tt * kXTileBytes;
-                            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c));
-                            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xt + xs_off(r, 4 * gs + 2 * c + 1));
-                            const f32x16 zero = {};
-                            f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), b_lo,
-                                                                               zero, 0, 0, 0);
-                            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), b_hi, d, 0, 0,
-                                                                        0);
 #pragma unroll
-                            for (int v = 0; v < nv; ++v) acc[tt][v] = __builtin_fma(scale, (double)d[v], acc[tt][v]);
+                            for (int v = 0; v < nv; ++v)
+                                acc[tt][v] = __builtin_fma(o.s[gs], (double)d[gs][tt][v], acc[tt][v]);
                         }
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                load_stage(b + 1, u, cur);
-                __builtin_amdgcn_sched_barrier(0);
             }
             if (live && b % nbt == nbt - 1) {
                 // the tile's last block: fold the remaining slices, store this strip
@@ -877,6 +985,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                         }
                 }
                 slice = 0;
+                next_bound = (int)kslice_begin(G, 1);
             }
         };
         for (int b = 0; b < nb; b += 2) {
