@@ -211,6 +211,56 @@ int w8_linear_swiglu_invariant_packed(const int8_t *Wp, const uint16_t *Sp, cons
                                       int64_t ldx, int64_t ldy, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Two projections of one activation batch, and the attention input projection.
+ *
+ * Source: the ninfer issue (GitHub issue 80), table "Where t selects
+ * arithmetic", row "attn_input_proj, linear_swiglu, linear_pair, linear_add
+ * (W8)".  The page names these fused decode ops without defining them; the
+ * readings here:
+ *
+ * w8_linear_pair_invariant: two projections of the same activations in one
+ *   launch, ya = w8_linear_invariant(Wa, Sa, x) and yb = w8_linear_invariant(Wb,
+ *   Sb, x), bit for bit (the launch's workgroups cover the row strips of both;
+ *   each output is the single call's computation).  Wa [Na, K], Wb [Nb, K] with
+ *   their scales; ya bf16 [t, ldya], yb bf16 [t, ldyb].  The rules and errors of
+ *   w8_linear_invariant apply to each projection; ya and yb must not overlap
+ *   each other or the inputs (not checked).  Always the LDS-staged split kernel.
+ * w8_attn_input_proj_invariant: the attention block's input projection, RMSNorm
+ *   of the hidden state followed by its (fused QKV) projection:
+ *     y = w8_linear_invariant(W_q, scales, w8i_rmsnorm(h, norm_weight, eps))
+ *   bit for bit.  h bf16 [t, ldh] (H features, 1 <= H <= 65536, 2-byte
+ *   aligned), norm_weight bf16 [H] or NULL (weight 1), W_q [N, H], y bf16
+ *   [t, ldy].  The normalised activations (bf16 [t, H] rows padded to a multiple
+ *   of 8) go to `workspace` (16-byte aligned, at least
+ *   w8_attn_input_proj_workspace_bytes(t, H) bytes; contents are scratch): one
+ *   call, two launches -- the norm's correctly rounded per-element division
+ *   runs once per element instead of once per projection workgroup.
+ * The _packed forms take weights from w8_pack (16-byte aligned) and give the
+ * same bits.
+ * ------------------------------------------------------------------------- */
+int w8_linear_pair_invariant(const int8_t *Wa, const uint16_t *Sa, const int8_t *Wb, const uint16_t *Sb,
+                             const uint16_t *x, int32_t t, int32_t T_pad, uint16_t *ya, uint16_t *yb,
+                             int64_t Na, int64_t Nb, int64_t K, int64_t ldx, int64_t ldya, int64_t ldyb,
+                             void *stream);
+
+int w8_linear_pair_invariant_packed(const int8_t *Wpa, const uint16_t *Spa, const int8_t *Wpb,
+                                    const uint16_t *Spb, const uint16_t *x, int32_t t, int32_t T_pad,
+                                    uint16_t *ya, uint16_t *yb, int64_t Na, int64_t Nb, int64_t K,
+                                    int64_t ldx, int64_t ldya, int64_t ldyb, void *stream);
+
+size_t w8_attn_input_proj_workspace_bytes(int32_t t, int64_t H);
+
+int w8_attn_input_proj_invariant(const uint16_t *h, const uint16_t *norm_weight, float eps,
+                                 const int8_t *W_q, const uint16_t *scales, int32_t t, int32_t T_pad,
+                                 uint16_t *y, int64_t N, int64_t H, int64_t ldh, int64_t ldy,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+int w8_attn_input_proj_invariant_packed(const uint16_t *h, const uint16_t *norm_weight, float eps,
+                                        const int8_t *Wp, const uint16_t *Sp, int32_t t, int32_t T_pad,
+                                        uint16_t *y, int64_t N, int64_t H, int64_t ldh, int64_t ldy,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Target-token logprob by fixed-width vocabulary blocks (LM-head epilogue).
  *
  * Source: the tokenspeed "Numerics envelopes" page, alignment.trainer table

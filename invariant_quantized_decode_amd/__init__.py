@@ -30,7 +30,9 @@ EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_by
            "w8_linear_add_invariant_packed", "w8_linear_swiglu_invariant_packed",
            "vocab_block_logprob_workspace_bytes", "vocab_block_logprob", "vocab_block_logprob_direct",
            "vocab_argmax_workspace_bytes", "vocab_argmax", "w8i_rmsnorm", "w8i_swiglu",
-           "w8i_residual_add", "w8i_exp32", "w8i_log32", "vocab_block_logprob_noalloc")
+           "w8i_residual_add", "w8i_exp32", "w8i_log32", "vocab_block_logprob_noalloc",
+           "w8_linear_pair_invariant", "w8_linear_pair_invariant_packed", "w8_attn_input_proj_workspace_bytes",
+           "w8_attn_input_proj_invariant", "w8_attn_input_proj_invariant_packed")
 
 
 class W8InvError(ValueError):
@@ -66,6 +68,15 @@ def _load():
     L.vocab_block_logprob.restype = ctypes.c_int
     L.vocab_block_logprob_direct.argtypes = [P, P, I32, P, I32, I64, I64, P, SZ, P]
     L.vocab_block_logprob_direct.restype = ctypes.c_int
+    L.w8_linear_pair_invariant.argtypes = [P, P, P, P, P, I32, I32, P, P, I64, I64, I64, I64, I64, I64, P]
+    L.w8_linear_pair_invariant_packed.argtypes = [P, P, P, P, P, I32, I32, P, P, I64, I64, I64, I64, I64, I64, P]
+    L.w8_attn_input_proj_workspace_bytes.argtypes = [I32, I64]
+    L.w8_attn_input_proj_workspace_bytes.restype = SZ
+    L.w8_attn_input_proj_invariant.argtypes = [P, P, F32, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
+    L.w8_attn_input_proj_invariant_packed.argtypes = [P, P, F32, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
+    for name in ("w8_linear_pair_invariant", "w8_linear_pair_invariant_packed", "w8_attn_input_proj_invariant",
+                 "w8_attn_input_proj_invariant_packed"):
+        getattr(L, name).restype = ctypes.c_int
     L.vocab_block_logprob_noalloc.argtypes = [P, P, I32, P, I32, I64, I64, P]
     L.vocab_block_logprob_noalloc.restype = ctypes.c_int
     L.vocab_argmax_workspace_bytes.argtypes, L.vocab_argmax_workspace_bytes.restype = [I32, I64], SZ
@@ -266,6 +277,88 @@ def w8_linear_swiglu_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: tor
                  _ptr(y), int(F), K, _row_major(x, "x"), _row_major(y, "y"))
     _check("w8_linear_swiglu_invariant_packed", st)
     return y
+
+
+def w8_linear_pair_invariant(Wa: torch.Tensor, Sa: torch.Tensor, Wb: torch.Tensor, Sb: torch.Tensor,
+                             x: torch.Tensor, t: int, T_pad: int, ya: torch.Tensor | None = None,
+                             yb: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Two projections of the same x in one launch: (w8_linear_invariant(Wa, Sa, x), w8_linear_invariant(Wb, Sb, x)),
+    bit for bit.  Wa int8 [Na, K], Wb int8 [Nb, K] with their fp16 scales; x bf16 [>=t, K]."""
+    Na, K, ldx, ya, ldya = _projection_args(Wa, Sa, x, t, ya, Wa.shape[0])
+    Nb, Kb, _, yb, ldyb = _projection_args(Wb, Sb, x, t, yb, Wb.shape[0])
+    if Kb != K:
+        raise ValueError("Wa and Wb must have the same K")
+    st = _launch(_lib.w8_linear_pair_invariant, Wa.device, _ptr(Wa), _ptr(Sa), _ptr(Wb), _ptr(Sb), _ptr(x), int(t),
+                 int(T_pad), _ptr(ya), _ptr(yb), Na, Nb, K, ldx, ldya, ldyb)
+    _check("w8_linear_pair_invariant", st)
+    return ya, yb
+
+
+def w8_linear_pair_invariant_packed(Wpa: torch.Tensor, Spa: torch.Tensor, Wpb: torch.Tensor, Spb: torch.Tensor,
+                                    x: torch.Tensor, t: int, T_pad: int, Na: int, Nb: int,
+                                    ya: torch.Tensor | None = None,
+                                    yb: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """w8_linear_pair_invariant over two projections in the packed layout (w8_pack of each); same bits."""
+    K, ya = _packed_args(Wpa, Spa, x, t, Na, Na, ya, Na)
+    _, yb = _packed_args(Wpb, Spb, x, t, Nb, Nb, yb, Nb)
+    st = _launch(_lib.w8_linear_pair_invariant_packed, Wpa.device, _ptr(Wpa), _ptr(Spa), _ptr(Wpb), _ptr(Spb),
+                 _ptr(x), int(t), int(T_pad), _ptr(ya), _ptr(yb), int(Na), int(Nb), K, _row_major(x, "x"),
+                 _row_major(ya, "ya"), _row_major(yb, "yb"))
+    _check("w8_linear_pair_invariant_packed", st)
+    return ya, yb
+
+
+def w8_attn_input_proj_workspace_bytes(t: int, H: int) -> int:
+    return int(_lib.w8_attn_input_proj_workspace_bytes(int(t), int(H)))
+
+
+def _attn_input_proj(packed, h, norm_weight, eps, W, S, t, T_pad, N, y, workspace):
+    if h.dtype != torch.bfloat16 or h.dim() != 2 or h.size(0) < t:
+        raise ValueError("h must be a bf16 [>=t, H] tensor")
+    H = h.size(1)
+    _dtype(norm_weight, "norm_weight", torch.bfloat16)
+    if norm_weight is not None and (norm_weight.numel() < H or not norm_weight.is_contiguous()):
+        raise ValueError("norm_weight must be a contiguous bf16 [H] tensor")
+    if y is None:
+        y = torch.empty((t, N), dtype=torch.bfloat16, device=h.device)
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.size(1) != N or y.size(0) < t:
+        raise ValueError(f"y must be a bf16 [>=t, {N}] tensor")
+    need = w8_attn_input_proj_workspace_bytes(t, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=h.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _same_gpu(("h", h), ("norm_weight", norm_weight), ("W", W), ("S", S), ("y", y), ("workspace", workspace))
+    fn = _lib.w8_attn_input_proj_invariant_packed if packed else _lib.w8_attn_input_proj_invariant
+    st = _launch(fn, h.device, _ptr(h), _ptr(norm_weight), float(eps), _ptr(W), _ptr(S), int(t), int(T_pad), _ptr(y),
+                 int(N), H, _row_major(h, "h"), _row_major(y, "y"), _ptr(workspace), workspace.numel())
+    _check("w8_attn_input_proj_invariant" + ("_packed" if packed else ""), st)
+    return y
+
+
+def w8_attn_input_proj_invariant(h: torch.Tensor, norm_weight: torch.Tensor | None, eps: float, W_q: torch.Tensor,
+                                 scales: torch.Tensor, t: int, T_pad: int, y: torch.Tensor | None = None,
+                                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[:t] = w8_linear_invariant(W_q, scales, w8i_rmsnorm(h, eps, norm_weight)) bit for bit (one call, the
+    normalised activations in `workspace`).  h bf16 [>=t, H]; W_q int8 [N, H]; scales fp16 [N, H/32]."""
+    if W_q.dtype != torch.int8 or W_q.dim() != 2 or not W_q.is_contiguous():
+        raise ValueError("W_q must be a contiguous int8 [N, H] tensor")
+    if scales.dtype not in (torch.float16, torch.int16) or tuple(scales.shape) != (W_q.shape[0], W_q.shape[1] // 32):
+        raise ValueError("scales must be fp16 [N, H/32]")
+    if W_q.shape[1] != h.size(1):
+        raise ValueError("W_q must have H columns")
+    return _attn_input_proj(False, h, norm_weight, eps, W_q, scales, t, T_pad, W_q.shape[0], y, workspace)
+
+
+def w8_attn_input_proj_invariant_packed(h: torch.Tensor, norm_weight: torch.Tensor | None, eps: float,
+                                        Wp: torch.Tensor, Sp: torch.Tensor, t: int, T_pad: int, N: int,
+                                        y: torch.Tensor | None = None,
+                                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """w8_attn_input_proj_invariant over weights packed by w8_pack (same bits)."""
+    wb, sb = w8_pack_bytes(N, h.size(1))
+    if Wp.dtype != torch.int8 or Wp.numel() != wb or Sp.numel() * 2 != sb:
+        raise ValueError("Wp / Sp must be the output of w8_pack for [N, H]")
+    return _attn_input_proj(True, h, norm_weight, eps, Wp, Sp, t, T_pad, int(N), y, workspace)
 
 
 def w8_linear_invariant_packed_kernel(N: int, K: int, T_pad: int) -> str:

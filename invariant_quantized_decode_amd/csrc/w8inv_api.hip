@@ -169,6 +169,85 @@ int w8_linear_swiglu_invariant_packed(const int8_t* Wp, const uint16_t* Sp, cons
     return linear_swiglu(true, Wp, Sp, x, t, T_pad, y, F, K, ldx, ldy, stream);
 }
 
+static int linear_pair(bool packed, const int8_t* Wa, const uint16_t* Sa, const int8_t* Wb, const uint16_t* Sb,
+                       const uint16_t* x, int32_t t, int32_t T_pad, uint16_t* ya, uint16_t* yb, int64_t Na, int64_t Nb,
+                       int64_t K, int64_t ldx, int64_t ldya, int64_t ldyb, void* stream) {
+    int st = check_projection(Wa, Sa, x, t, T_pad, ya, Na, K, ldx, ldya, Na);
+    if (st != W8I_OK || t == 0) return st;
+    st = check_projection(Wb, Sb, x, t, T_pad, yb, Nb, K, ldx, ldyb, Nb);
+    if (st != W8I_OK) return st;
+    if (packed && (packed_weight_bytes(Na, K) >= ((int64_t)1 << 32) || packed_weight_bytes(Nb, K) >= ((int64_t)1 << 32)))
+        return W8I_ESHAPE;
+    if (packed && (!aligned(Sa, 16) || !aligned(Sb, 16))) return W8I_EALIGN;
+    LinearEpilogue ep;
+    ep.W2 = Wb;
+    ep.S2 = Sb;
+    ep.Y2 = yb;
+    ep.N2 = Nb;
+    ep.ldy2 = ldyb;
+    return launch_linear_pair(packed, Wa, Sa, x, t, T_pad, ya, Na, K, ldx, ldya, ep, as_stream(stream));
+}
+
+int w8_linear_pair_invariant(const int8_t* Wa, const uint16_t* Sa, const int8_t* Wb, const uint16_t* Sb,
+                             const uint16_t* x, int32_t t, int32_t T_pad, uint16_t* ya, uint16_t* yb, int64_t Na,
+                             int64_t Nb, int64_t K, int64_t ldx, int64_t ldya, int64_t ldyb, void* stream) {
+    return linear_pair(false, Wa, Sa, Wb, Sb, x, t, T_pad, ya, yb, Na, Nb, K, ldx, ldya, ldyb, stream);
+}
+
+int w8_linear_pair_invariant_packed(const int8_t* Wpa, const uint16_t* Spa, const int8_t* Wpb, const uint16_t* Spb,
+                                    const uint16_t* x, int32_t t, int32_t T_pad, uint16_t* ya, uint16_t* yb,
+                                    int64_t Na, int64_t Nb, int64_t K, int64_t ldx, int64_t ldya, int64_t ldyb,
+                                    void* stream) {
+    return linear_pair(true, Wpa, Spa, Wpb, Spb, x, t, T_pad, ya, yb, Na, Nb, K, ldx, ldya, ldyb, stream);
+}
+
+// the normalised activations of attn_input_proj: bf16 [t, round_up(H, 8)], 16-byte aligned rows
+static int64_t attn_norm_ld(int64_t H) { return (H + 7) / 8 * 8; }
+
+size_t w8_attn_input_proj_workspace_bytes(int32_t t, int64_t H) {
+    if (t <= 0 || H < 1 || H > 65536) return 0;
+    return (size_t)(((int64_t)t * attn_norm_ld(H) * 2 + 255) / 256 * 256);
+}
+
+static int attn_input_proj(bool packed, const uint16_t* h, const uint16_t* norm_weight, float eps,
+                           const int8_t* W, const uint16_t* S, int32_t t, int32_t T_pad, uint16_t* y, int64_t N,
+                           int64_t H, int64_t ldh, int64_t ldy, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return W8I_ET;
+    if (t < 0 || t > T_pad) return W8I_ET;
+    if (t == 0) return W8I_OK;
+    if (!h) return W8I_ENULL;
+    if (H < 1 || H > 65536 || ldh < H) return W8I_ESHAPE;
+    if (!aligned(h, 2) || (norm_weight && !aligned(norm_weight, 2))) return W8I_EALIGN;
+    if (!workspace || workspace_bytes < w8_attn_input_proj_workspace_bytes(t, H)) return W8I_EWORKSPACE;
+    if (!aligned(workspace, 16)) return W8I_EALIGN;
+    uint16_t* xn = static_cast<uint16_t*>(workspace);
+    const int64_t ldn = attn_norm_ld(H);
+    int st = check_projection(W, S, xn, t, T_pad, y, N, H, ldn, ldy, N);
+    if (st != W8I_OK) return st;
+    if (packed && packed_weight_bytes(N, H) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (packed && !aligned(S, 16)) return W8I_EALIGN;
+    st = launch_rmsnorm(h, norm_weight, eps, xn, t, H, ldh, ldn, as_stream(stream));
+    if (st != W8I_OK) return st;
+    return packed ? launch_linear_packed(W, S, xn, t, T_pad, y, N, H, ldn, ldy, as_stream(stream))
+                  : launch_linear(W, S, xn, t, T_pad, y, N, H, ldn, ldy, as_stream(stream));
+}
+
+int w8_attn_input_proj_invariant(const uint16_t* h, const uint16_t* norm_weight, float eps, const int8_t* W_q,
+                                 const uint16_t* scales, int32_t t, int32_t T_pad, uint16_t* y, int64_t N, int64_t H,
+                                 int64_t ldh, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    return attn_input_proj(false, h, norm_weight, eps, W_q, scales, t, T_pad, y, N, H, ldh, ldy, workspace,
+                           workspace_bytes, stream);
+}
+
+int w8_attn_input_proj_invariant_packed(const uint16_t* h, const uint16_t* norm_weight, float eps, const int8_t* Wp,
+                                        const uint16_t* Sp, int32_t t, int32_t T_pad, uint16_t* y, int64_t N,
+                                        int64_t H, int64_t ldh, int64_t ldy, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    return attn_input_proj(true, h, norm_weight, eps, Wp, Sp, t, T_pad, y, N, H, ldh, ldy, workspace,
+                           workspace_bytes, stream);
+}
+
 size_t vocab_block_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) {
     if (t <= 0 || V <= 0 || block < 256 || block > 32768 || (block & (block - 1)) != 0) return 0;
     return logprob_workspace_bytes(t, V, block);

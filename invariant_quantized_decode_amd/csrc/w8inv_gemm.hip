@@ -173,10 +173,24 @@ __device__ __forceinline__ void wait_vm() {
 // R: output rows per workgroup (8..32; 32 with the SwiGLU epilogue).  The
 // matrix core always computes 32 rows; rows R..31 repeat row R - 1's loads
 // (no extra memory traffic) and are not stored.
+// EPI kEpiPair: the launch covers two projections of the same x, the first
+// ep.wg1 workgroups the first (W, S, Y, N, ldy), the others the second (ep.W2,
+// ...); each workgroup then runs exactly the single projection's code.
 template <int TP16, int D, bool LS, int EPI, bool PK>  // TP16 = T_pad / 16 (1..4), D = ring depth (2..4)
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, LinearEpilogue ep, int R) {
+    int bid = (int)blockIdx.x;
+    if constexpr (EPI == kEpiPair) {
+        if (bid >= ep.wg1) {
+            W = ep.W2;
+            S = ep.S2;
+            Y = ep.Y2;
+            N = ep.N2;
+            ldy = ep.ldy2;
+            bid -= ep.wg1;
+        }
+    }
     static_assert(TP16 >= 1 && TP16 <= 4, "T_pad 16..64");
     static_assert(D >= 2 && D <= 4, "ring depth");
     constexpr int NT = (TP16 + 1) / 2;                // 32-column tiles
@@ -198,12 +212,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = (int)(K / kGroup);
-    const int64_t n0 = (int64_t)blockIdx.x * R;
+    const int64_t n0 = (int64_t)bid * R;
     // The workgroup's rows: n0 .. n0 + R - 1, or with the SwiGLU epilogue the
     // 16 gate rows h0 .. h0 + 15 followed by the 16 matching up rows
     // F + h0 .. F + h0 + 15.  Rows past the end read the last valid row (valid
     // memory; their results are never stored).
-    const int64_t h0 = (int64_t)blockIdx.x * (kRows / 2);
+    const int64_t h0 = (int64_t)bid * (kRows / 2);
     auto row_of = [&](int rho) -> int64_t {
         if constexpr (EPI == kEpiSwiGLU) {
             const int64_t h = h0 + (rho & 15);
@@ -1157,7 +1171,10 @@ static int launch_split(const LinearPlan& p, const int8_t* W, const uint16_t* S,
                         uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                         hipStream_t stream) {
     const int R = EPI == kEpiSwiGLU ? kRows : p.rows;
-    const int64_t wgs = EPI == kEpiSwiGLU ? (ep.F + kRows / 2 - 1) / (kRows / 2) : (N + R - 1) / R;
+    if constexpr (EPI == kEpiPair) ep.wg1 = (int)((N + R - 1) / R);
+    const int64_t wgs = EPI == kEpiSwiGLU ? (ep.F + kRows / 2 - 1) / (kRows / 2)
+                        : EPI == kEpiPair ? ep.wg1 + (ep.N2 + R - 1) / R
+                                          : (N + R - 1) / R;
     const dim3 grid((unsigned)wgs);
     const dim3 block(kGemmThreads);
 #define W8I_SPLIT_LAUNCH(TP, D, LS)                                                                     \
@@ -1215,6 +1232,23 @@ int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X
         return launch_tiles(Wp, Sp, X, t, T_pad, Y, N, K, ldx, ldy, 2, stream);
     const LinearPlan p = plan_packed(T_pad / 16, (N + kRows - 1) / kRows);
     return launch_split<kEpiStore, true>(p, Wp, Sp, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
+}
+
+int launch_linear_pair(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
+                       uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+                       hipStream_t stream) {
+    // the split kernel, planned for the two projections together: rows per
+    // workgroup from their total rows; scales staged in LDS only when both
+    // scale arrays allow it
+    T_pad = kernel_width(t, T_pad);
+    if (packed) {
+        const LinearPlan p = plan_packed(T_pad / 16, (N + kRows - 1) / kRows + (ep.N2 + kRows - 1) / kRows);
+        return launch_split<kEpiPair, true>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
+    }
+    const bool s16 = (reinterpret_cast<uintptr_t>(S) & 15) == 0 && (reinterpret_cast<uintptr_t>(ep.S2) & 15) == 0;
+    LinearPlan p = plan_split(T_pad / 16, s16 ? round_dma(64 * (K / kGroup)) : 0);
+    p.rows = plain_rows_per_workgroup(N + ep.N2);
+    return launch_split<kEpiPair>(p, W, S, X, t, Y, N, K, ldx, ldy, ep, stream);
 }
 
 int launch_linear_epilogue(int epi, bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,

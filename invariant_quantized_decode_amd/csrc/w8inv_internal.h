@@ -31,10 +31,19 @@ __host__ __device__ __forceinline__ int64_t kslice_begin(int64_t G, int i) {
 constexpr int kEpiStore = 0;   // y = bf16(W x)
 constexpr int kEpiAdd = 1;     // y = residual add of bf16(W x) and r (the glue's w8i_residual_add)
 constexpr int kEpiSwiGLU = 2;  // rows [0, F) gate, [F, 2F) up; y[:, h] = SwiGLU(gate h, up h) (w8i_swiglu)
+constexpr int kEpiPair = 3;    // two projections of one x: workgroups [0, wg1) the first, the rest the second
 struct LinearEpilogue {
-    const uint16_t* r;  // kEpiAdd: residual, bf16 [t, ldr]
-    int64_t ldr;
-    int64_t F;          // kEpiSwiGLU: gate rows (the projection has 2F rows)
+    const uint16_t* r = nullptr;  // kEpiAdd: residual, bf16 [t, ldr]
+    int64_t ldr = 0;
+    int64_t F = 0;                // kEpiSwiGLU: gate rows (the projection has 2F rows)
+    // kEpiPair: the second projection (weights, scales, output, rows, output stride) and the
+    // number of workgroups of the first (set by the launcher)
+    const int8_t* W2 = nullptr;
+    const uint16_t* S2 = nullptr;
+    uint16_t* Y2 = nullptr;
+    int64_t N2 = 0;
+    int64_t ldy2 = 0;
+    int wg1 = 0;
 };
 
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
@@ -53,6 +62,11 @@ int launch_pack(const int8_t* W, const uint16_t* S, int64_t N, int64_t K, int8_t
 int launch_linear_epilogue(int epi, bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t,
                            int T_pad, uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
                            hipStream_t stream);
+// two projections of one x in one launch (the split kernel, kEpiPair): ep carries the second
+// projection (W2, S2, Y2, N2, ldy2); `packed`: both in the packed layout
+int launch_linear_pair(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
+                       uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, LinearEpilogue ep,
+                       hipStream_t stream);
 const char* linear_kernel_name(int64_t N, int64_t K, int T_pad, const void* S);
 const char* linear_packed_kernel_name(int64_t N, int64_t K, int T_pad);
 

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 29
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -198,6 +198,32 @@ def test_noalloc_logprob_validation():
     assert L.vocab_block_logprob_workspace_bytes(64, 1 << 22, 256) > 1 << 20
     assert f(fake(A), fake(A), 256, fake(A), 64, 1 << 22, 1 << 22, None) == -8
     assert L.w8i_status_string(-8).decode().startswith("W8I_ESCRATCH")
+
+
+def test_pair_and_attn_input_proj_validation():
+    """linear_pair checks both projections' operands; attn_input_proj checks the norm's input, the
+    workspace and the projection, all before any device access."""
+    f = L.w8_linear_pair_invariant
+    ok = (fake(A), fake(A), fake(A), fake(A), fake(A), 4, 32, fake(A), fake(A), 64, 32, 256, 256, 64, 32, None)
+    assert f(*ok[:5], 0, 32, None, None, 64, 32, 256, 256, 64, 32, None) == 0          # t == 0
+    assert f(*ok[:5], 4, 24, *ok[7:]) == -4                                             # T_pad
+    assert f(fake(A), fake(A), None, fake(A), *ok[4:]) == -1                            # Wb NULL
+    assert f(*ok[:9], 64, 32, 256, 256, 64, 16, None) == -2                             # ldyb < Nb
+    assert f(*ok[:2], fake(A + 8), *ok[3:]) == -3                                       # Wb misaligned
+    assert L.w8_linear_pair_invariant_packed(fake(A), fake(A), fake(A), fake(A + 2), *ok[4:]) == -3  # Spb
+    g = L.w8_attn_input_proj_invariant
+    need = L.w8_attn_input_proj_workspace_bytes(32, 5120)
+    assert need == 32 * 5120 * 2
+    assert L.w8_attn_input_proj_workspace_bytes(3, 100) == 768 and L.w8_attn_input_proj_workspace_bytes(3, 70000) == 0
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(  # noqa: E731
+        h=fake(A), w=None, eps=ctypes.c_float(1e-6), W=fake(A), S=fake(A), t=4, T=32, y=fake(A), N=7168, H=5120,
+        ldh=5120, ldy=7168, ws=fake(A), wsb=L.w8_attn_input_proj_workspace_bytes(4, 5120), st=None).items()]
+    need = L.w8_attn_input_proj_workspace_bytes(4, 5120)
+    assert g(*args()) != -6 and g(*args(t=0, h=None, W=None)) == 0
+    assert g(*args(ws=None)) == -6 and g(*args(wsb=need - 2)) == -6 and g(*args(ws=fake(A + 8))) == -3
+    assert g(*args(h=None)) == -1 and g(*args(H=70000, ldh=70000)) == -2 and g(*args(ldh=100)) == -2
+    assert g(*args(H=5100, ldh=5100)) == -2           # the projection's K = H must be a multiple of 32
+    assert g(*args(T=40)) == -4 and g(*args(W=None)) == -1
 
 
 def test_glue_and_hooks_reject_invalid_arguments():
