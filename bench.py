@@ -209,6 +209,7 @@ def headline(torch, w8, synth, dev, args):
     n_logits = max(1, math.ceil(GIB / (T_pad * N * 2)))  # logits buffers rotating over >= 1 GiB
     Ls = [torch.empty((T_pad, N), dtype=torch.bfloat16, device=dev) for _ in range(n_logits)]
     ws = torch.empty(w8.vocab_block_logprob_workspace_bytes(T_pad, N, block), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(w8.w8_head_logprob_workspace_bytes(T_pad, N, block), dtype=torch.uint8, device=dev)
     out = torch.empty(T_pad, dtype=torch.float32, device=dev)
     kernel = w8.w8_linear_invariant_packed_kernel(N, K, T_pad)
     kernel_plain = w8.w8_linear_invariant_kernel(N, K, T_pad, S0)
@@ -221,12 +222,18 @@ def headline(torch, w8, synth, dev, args):
     def logprob(lg, tg, t):
         return w8.vocab_block_logprob(lg, tg, block, out=out, t=t, workspace=ws)
 
+    def fused(Xt, tg, t, lg):
+        # the head projection with the logprob's row-max pass fused into it, then the logprob's
+        # block partials and fold (w8_head_logprob_invariant_packed): the same bits as project + logprob
+        return w8.w8_head_logprob_invariant_packed(Wp, Sp, Xt, tg, t, T_pad, block, N, logits=lg, out=out,
+                                                   workspace=ws_f)
+
     # ---- t-invariance on this workload, before any timing: for t = 1..32 a random ordered subset of the
     # 32 pool columns keeps the logits bits and the logprob bits it has in the identity-order t = 32 run,
     # on both layouts (the plain layout at t = 32 and at every fourth t)
     base = project("packed", X, T_pad, None).clone()
     base_lp = w8.vocab_block_logprob(base, Tg, block).clone()
-    inv = {"logits": True, "logprob": True, "plain_layout": True}
+    inv = {"logits": True, "logprob": True, "plain_layout": True, "fused": True}
     for t in range(1, T_pad + 1):
         cols = torch.from_numpy(d["perms"][t]).to(dev)
         Xc = X[cols].contiguous()
@@ -237,6 +244,9 @@ def headline(torch, w8, synth, dev, args):
         if t % 4 == 0 or t == 1:
             yp = project("plain", Xc, t, None)
             inv["plain_layout"] &= bool(torch.equal(yp.view(torch.int16), base[cols].view(torch.int16)))
+        fl, fo = w8.w8_head_logprob_invariant_packed(Wp, Sp, Xc, Tg[cols].contiguous(), t, T_pad, block, N)
+        inv["fused"] &= bool(torch.equal(fl.view(torch.int16), base[cols].view(torch.int16))) and \
+            bool(torch.equal(fo.view(torch.int32), base_lp[cols].view(torch.int32)))
     torch.cuda.synchronize()
     inv_ok = all(inv.values())
 
@@ -247,6 +257,12 @@ def headline(torch, w8, synth, dev, args):
         def make(i):
             lg = Ls[i % n_logits]
             return lambda: (project("packed", X[:t], t, lg), logprob(lg, Tg, t))
+        return make
+
+    def fused_call(t):
+        def make(i):
+            lg = Ls[i % n_logits]
+            return lambda: fused(X[:t], Tg, t, lg)
         return make
 
     def gemm_call(layout, t):
@@ -265,6 +281,7 @@ def headline(torch, w8, synth, dev, args):
     # the contract's timed region: exactly --steps steps at t = T_pad (warm-up before it)
     step = {T_pad: timer.measure(step_call(T_pad), steps=args.steps, warmup=args.warmup, label=f"step t={T_pad}")}
     step[1] = timer.measure(step_call(1), warmup=args.warmup, label="step t=1")
+    fstep = {t: timer.measure(fused_call(t), warmup=args.warmup, label=f"fused step t={t}") for t in (T_pad, 1)}
     gemm = {t: timer.measure(gemm_call("packed", t), warmup=args.warmup, label=f"projection t={t}")
             for t in (T_pad, 1)}
     # every logits buffer holds a full projection before the logprob is timed on its own (cold: the
@@ -378,6 +395,12 @@ def headline(torch, w8, synth, dev, args):
                "tflops_useful": r(2.0 * N * K / (st1 * 1e-6) / 1e12),
                "tflops_executed": r(2.0 * N * K * T_pad / (st1 * 1e-6) / 1e12), "spread": spread(step[1])},
         "step": {"t_pad": step_rec[T_pad], "t1": step_rec[1]},
+        "fused_step": {"call": "w8_head_logprob_invariant_packed (head projection with the row-max pass fused, "
+                               "then block partials and fold; the same bits)",
+                       "t_pad": {"us": r(fstep[T_pad]["us"]), "weight_gbs": r(gbs(wbytes, fstep[T_pad]["us"]), 1),
+                                 "spread": spread(fstep[T_pad])},
+                       "t1": {"us": r(fstep[1]["us"]), "weight_gbs": r(gbs(wbytes, fstep[1]["us"]), 1),
+                              "spread": spread(fstep[1])}},
         "kernels": {"head_projection": {"kernel": kernel, "t_pad_us": r(g32), "t1_us": r(g1)},
                     "logprob": {"kernels": "lp_block_max + lp_block_sumexp + lp_fold", "t_pad": lp_rec[T_pad],
                                 "t1": lp_rec[1]}},

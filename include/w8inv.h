@@ -308,6 +308,44 @@ int vocab_block_logprob_direct(const uint16_t *logits, const int64_t *targets, i
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The LM head fused with the blockwise logprob's row maximum.
+ *
+ * Source: tokenspeed numerics, "Logprobs" section and the block_sumexp leaf
+ * contract paragraph (the row max is taken first, every block partial is then
+ * formed from logits shifted by it); the projection as for
+ * w8_linear_invariant.  The fixed arithmetic needs the row's global maximum
+ * before any block partial, so only that first pass can join the head
+ * projection: its workgroups write, with the logits, the column maxima of
+ * each 256-row tile they store (exact in any order), and the logprob's
+ * block-partial and fold kernels take the row maximum from those per-tile
+ * maxima instead of a pass over the logits.
+ *
+ *   logits = w8_linear_invariant(W_q, scales, x, t, T_pad)        bit for bit
+ *   out    = vocab_block_logprob(logits, targets, block)          bit for bit
+ *
+ * Operands as for the two calls: W_q int8 [V, K] (V output rows = the
+ * vocabulary), scales fp16 [V, K/32], x bf16 [t, ldx], logits bf16 [t, ldl]
+ * (ldl >= V; written), targets int64 [t], block a power of two in
+ * [256, 32768], out fp32 [t].  The projection always runs the persistent
+ * kernel (the one w8_linear_invariant runs for N >= 131072 at T_pad <= 32):
+ * T_pad 16 or 32, or 48 / 64 with t <= 32 (W8I_ET otherwise).  workspace:
+ * 16-byte aligned, at least w8_head_logprob_workspace_bytes(t, V, block)
+ * bytes (per-tile maxima [t, ceil(V/256)] and block partials [t, ceil(V/block)]
+ * in fp32); contents are scratch.  The _packed form takes w8_pack's layout.
+ * ------------------------------------------------------------------------- */
+size_t w8_head_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block);
+
+int w8_head_logprob_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_t *x,
+                              const int64_t *targets, int32_t t, int32_t T_pad, int32_t block,
+                              uint16_t *logits, float *out, int64_t V, int64_t K, int64_t ldx, int64_t ldl,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+int w8_head_logprob_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint16_t *x,
+                                     const int64_t *targets, int32_t t, int32_t T_pad, int32_t block,
+                                     uint16_t *logits, float *out, int64_t V, int64_t K, int64_t ldx,
+                                     int64_t ldl, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Canonical greedy argmax of each column (LM-head epilogue).
  *
  * Source: tokenspeed numerics, "Logprobs" section: the vocabulary-parallel

@@ -32,7 +32,8 @@ EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_by
            "vocab_argmax_workspace_bytes", "vocab_argmax", "w8i_rmsnorm", "w8i_swiglu",
            "w8i_residual_add", "w8i_exp32", "w8i_log32", "vocab_block_logprob_noalloc",
            "w8_linear_pair_invariant", "w8_linear_pair_invariant_packed", "w8_attn_input_proj_workspace_bytes",
-           "w8_attn_input_proj_invariant", "w8_attn_input_proj_invariant_packed")
+           "w8_attn_input_proj_invariant", "w8_attn_input_proj_invariant_packed", "w8_head_logprob_workspace_bytes",
+           "w8_head_logprob_invariant", "w8_head_logprob_invariant_packed")
 
 
 class W8InvError(ValueError):
@@ -76,6 +77,11 @@ def _load():
     L.w8_attn_input_proj_invariant_packed.argtypes = [P, P, F32, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
     for name in ("w8_linear_pair_invariant", "w8_linear_pair_invariant_packed", "w8_attn_input_proj_invariant",
                  "w8_attn_input_proj_invariant_packed"):
+        getattr(L, name).restype = ctypes.c_int
+    L.w8_head_logprob_workspace_bytes.argtypes = [I32, I64, I32]
+    L.w8_head_logprob_workspace_bytes.restype = SZ
+    for name in ("w8_head_logprob_invariant", "w8_head_logprob_invariant_packed"):
+        getattr(L, name).argtypes = [P, P, P, P, I32, I32, I32, P, P, I64, I64, I64, I64, P, SZ, P]
         getattr(L, name).restype = ctypes.c_int
     L.vocab_block_logprob_noalloc.argtypes = [P, P, I32, P, I32, I64, I64, P]
     L.vocab_block_logprob_noalloc.restype = ctypes.c_int
@@ -359,6 +365,65 @@ def w8_attn_input_proj_invariant_packed(h: torch.Tensor, norm_weight: torch.Tens
     if Wp.dtype != torch.int8 or Wp.numel() != wb or Sp.numel() * 2 != sb:
         raise ValueError("Wp / Sp must be the output of w8_pack for [N, H]")
     return _attn_input_proj(True, h, norm_weight, eps, Wp, Sp, t, T_pad, int(N), y, workspace)
+
+
+def w8_head_logprob_workspace_bytes(t: int, V: int, block: int) -> int:
+    return int(_lib.w8_head_logprob_workspace_bytes(int(t), int(V), int(block)))
+
+
+def _head_logprob(packed, W, S, x, targets, t, T_pad, block, V, K, logits, out, workspace):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.size(1) != K or x.size(0) < t:
+        raise ValueError("x must be a bf16 [>=t, K] tensor")
+    if targets.dtype != torch.int64 or targets.numel() < t or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int64 [t] tensor")
+    if logits is None:
+        logits = torch.empty((t, V), dtype=torch.bfloat16, device=x.device)
+    if logits.dtype != torch.bfloat16 or logits.dim() != 2 or logits.size(1) != V or logits.size(0) < t:
+        raise ValueError(f"logits must be a bf16 [>=t, {V}] tensor")
+    if out is None:
+        out = torch.empty(t, dtype=torch.float32, device=x.device)
+    _dtype(out, "out", torch.float32)
+    if out.numel() < t or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [t] tensor")
+    need = w8_head_logprob_workspace_bytes(t, V, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _same_gpu(("W", W), ("S", S), ("x", x), ("targets", targets), ("logits", logits), ("out", out),
+              ("workspace", workspace))
+    fn = _lib.w8_head_logprob_invariant_packed if packed else _lib.w8_head_logprob_invariant
+    st = _launch(fn, x.device, _ptr(W), _ptr(S), _ptr(x), _ptr(targets), int(t), int(T_pad), int(block), _ptr(logits),
+                 _ptr(out), int(V), int(K), _row_major(x, "x"), _row_major(logits, "logits"), _ptr(workspace),
+                 workspace.numel())
+    _check("w8_head_logprob_invariant" + ("_packed" if packed else ""), st)
+    return logits, out
+
+
+def w8_head_logprob_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, targets: torch.Tensor, t: int,
+                              T_pad: int, block: int, logits: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """(logits, logprob): the LM head w8_linear_invariant(W_q, scales, x) fused with the row-max pass of
+    vocab_block_logprob(logits, targets, block); both bit for bit the unfused results."""
+    if W_q.dtype != torch.int8 or W_q.dim() != 2 or not W_q.is_contiguous():
+        raise ValueError("W_q must be a contiguous int8 [V, K] tensor")
+    V, K = W_q.shape
+    if scales.dtype not in (torch.float16, torch.int16) or tuple(scales.shape) != (V, K // 32):
+        raise ValueError("scales must be fp16 [V, K/32]")
+    return _head_logprob(False, W_q, scales, x, targets, t, T_pad, block, V, K, logits, out, workspace)
+
+
+def w8_head_logprob_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, targets: torch.Tensor,
+                                     t: int, T_pad: int, block: int, V: int, logits: torch.Tensor | None = None,
+                                     out: torch.Tensor | None = None,
+                                     workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """w8_head_logprob_invariant over the head's weights packed by w8_pack (same bits)."""
+    K = x.size(1)
+    wb, sb = w8_pack_bytes(V, K)
+    if Wp.dtype != torch.int8 or Wp.numel() != wb or Sp.numel() * 2 != sb:
+        raise ValueError("Wp / Sp must be the output of w8_pack for [V, K]")
+    return _head_logprob(True, Wp, Sp, x, targets, t, T_pad, block, int(V), K, logits, out, workspace)
 
 
 def w8_linear_invariant_packed_kernel(N: int, K: int, T_pad: int) -> str:

@@ -285,6 +285,45 @@ int vocab_block_logprob_direct(const uint16_t* logits, const int64_t* targets, i
     return block_logprob(logits, targets, block, out, t, V, ldl, workspace, workspace_bytes, true, stream);
 }
 
+size_t w8_head_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block) {
+    if (t <= 0 || V <= 0 || V > kMaxDim || block < 256 || block > 32768 || (block & (block - 1)) != 0) return 0;
+    return logprob_from_max_workspace_bytes(t, V, block, tiles_of(V));
+}
+
+static int head_logprob(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* x, const int64_t* targets,
+                        int32_t t, int32_t T_pad, int32_t block, uint16_t* logits, float* out, int64_t V, int64_t K,
+                        int64_t ldx, int64_t ldl, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_projection(W, S, x, t, T_pad, logits, V, K, ldx, ldl, V);
+    if (st != W8I_OK || t == 0) return st;
+    if (T_pad > 32 && t > 32) return W8I_ET;
+    if (packed && packed_weight_bytes(V, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
+    if (packed && !aligned(S, 16)) return W8I_EALIGN;
+    st = check_logprob(logits, targets, block, out, t, V, ldl);
+    if (st != W8I_OK) return st;
+    if (!workspace || workspace_bytes < w8_head_logprob_workspace_bytes(t, V, block)) return W8I_EWORKSPACE;
+    if (!aligned(workspace, 16)) return W8I_EALIGN;
+    st = launch_linear_max(packed, W, S, x, t, T_pad, logits, V, K, ldx, ldl, static_cast<float*>(workspace),
+                           as_stream(stream));
+    if (st != W8I_OK) return st;
+    return launch_logprob_from_max(logits, targets, block, out, t, V, ldl, workspace, tiles_of(V), as_stream(stream));
+}
+
+int w8_head_logprob_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const int64_t* targets,
+                              int32_t t, int32_t T_pad, int32_t block, uint16_t* logits, float* out, int64_t V,
+                              int64_t K, int64_t ldx, int64_t ldl, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    return head_logprob(false, W_q, scales, x, targets, t, T_pad, block, logits, out, V, K, ldx, ldl, workspace,
+                        workspace_bytes, stream);
+}
+
+int w8_head_logprob_invariant_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* x, const int64_t* targets,
+                                     int32_t t, int32_t T_pad, int32_t block, uint16_t* logits, float* out, int64_t V,
+                                     int64_t K, int64_t ldx, int64_t ldl, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    return head_logprob(true, Wp, Sp, x, targets, t, T_pad, block, logits, out, V, K, ldx, ldl, workspace,
+                        workspace_bytes, stream);
+}
+
 int vocab_block_logprob_noalloc(const uint16_t* logits, const int64_t* targets, int32_t block, float* out, int32_t t,
                                 int64_t V, int64_t ldl, void* stream) {
     const int st = check_logprob(logits, targets, block, out, t, V, ldl);

@@ -687,10 +687,18 @@ constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
 
 // PK: packed layout (w8_pack): each stage's weights are the strip's 2 KB block
 // and its scales one 128-byte line, loaded with the stage.
-template <int TP16, bool SC, bool PK>
+// MX: the logprob's max epilogue (the head projection fused with the first
+// step of the blockwise logprob): besides storing the tile's outputs, the
+// workgroup writes, for every live column j, the maximum over the tile's rows
+// n < N of the stored values (bf16 widened exactly to fp32), or NaN if one of
+// them is NaN, to M[j * ldm + tile].  A maximum is exact in any order, so the
+// row maximum the logprob takes from these per-tile maxima is the one it would
+// take from the logits.
+template <int TP16, bool SC, bool PK, bool MX = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, int ntiles) {
+    uint16_t* __restrict__ Y, int64_t N, int64_t K, int t, int64_t ldx, int64_t ldy, int ntiles,
+    float* __restrict__ M, int64_t ldm) {
     constexpr int NT = (TP16 + 1) / 2;
     constexpr int kLastValues = (TP16 & 1) ? 8 : 16;
     constexpr int kBlockStages = PK ? 8 : 4;                      // stages per block (BS)
@@ -706,6 +714,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // one array per buffer, so each buffer's direct loads are told apart
     __shared__ __align__(16) unsigned char xb0[kBlockBytes];
     __shared__ __align__(16) unsigned char xb1[kBlockBytes];
+    // MX: each wave's column maxima of its strip (value, NaN flag), per 32-column tile
+    __shared__ float smax[MX ? kTileStrips * 32 * NT : 1];
+    __shared__ int snan[MX ? kTileStrips * 32 * NT : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -998,6 +1009,50 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                             if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(total[tt][v]);
                         }
                 }
+                if constexpr (MX) {
+                    // lane (r, c) holds row r of the strip for columns 8 (v / 4) + 4 c + v % 4:
+                    // reduce over the 32 lanes of each half (xor 1 .. 16 keeps c), so that
+                    // lanes 0 and 32 hold the strip's column maxima; the 8 strips meet in LDS
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                        for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
+                            const float val = bf16_to_f32(f64_to_bf16(total[tt][v]));
+                            float m = n < N && val == val ? val : -__builtin_inff();
+                            int nan = n < N && val != val ? 1 : 0;
+#pragma unroll
+                            for (int off = 1; off < 32; off <<= 1) {
+                                m = __builtin_fmaxf(m, __shfl_xor(m, off));
+                                nan |= __shfl_xor(nan, off);
+                            }
+                            const int j = 8 * (v >> 2) + 4 * c + (v & 3);
+                            if (r == 0) {
+                                smax[(wave * NT + tt) * 32 + j] = m;
+                                snan[(wave * NT + tt) * 32 + j] = nan;
+                            }
+                        }
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    if (wave == 0) {
+                        // lane l: column l of each tile
+#pragma unroll
+                        for (int tt = 0; tt < NT; ++tt) {
+                            const int j = 32 * tt + (lane & 31);
+                            float m = -__builtin_inff();
+                            int nan = 0;
+#pragma unroll
+                            for (int w = 0; w < kTileStrips; ++w) {
+                                m = __builtin_fmaxf(m, smax[(w * NT + tt) * 32 + (lane & 31)]);
+                                nan |= snan[(w * NT + tt) * 32 + (lane & 31)];
+                            }
+                            if (lane < 32 && j < t) M[(int64_t)j * ldm + b / nbt * (int)gridDim.x + (int)blockIdx.x] =
+                                                         nan ? __builtin_nanf("") : m;
+                        }
+                    }
+                }
                 slice = 0;
                 next_bound = (int)kslice_begin(G, 1);
             }
@@ -1026,17 +1081,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
 static int tile_count(int64_t N) { return (int)((N + kTileStrips * kRows - 1) / (kTileStrips * kRows)); }
 
 // scales: 0 per-stage 2-byte loads, 1 eight scales per 16-byte load (SC), 2 packed layout (PK)
+// M != nullptr: the max epilogue (MX), per-tile column maxima into M [t][ldm = tile count]
 static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
-                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, int scales, hipStream_t stream) {
+                        int64_t N, int64_t K, int64_t ldx, int64_t ldy, int scales, hipStream_t stream,
+                        float* M = nullptr) {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return W8I_EHIP;
     const int ntiles = tile_count(N);
     const dim3 grid((unsigned)(ntiles < ncu ? ntiles : ncu)), block(kGemmThreads);
-#define W8I_TILES_LAUNCH(TP, SCV, PKV)                                                                    \
-    hipLaunchKernelGGL((gemm_w8g32_tiles<TP, SCV, PKV>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, \
-                       ntiles)
+#define W8I_TILES_LAUNCH(TP, SCV, PKV)                                                                            \
+    if (M)                                                                                                        \
+        hipLaunchKernelGGL((gemm_w8g32_tiles<TP, SCV, PKV, true>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, \
+                           ldy, ntiles, M, (int64_t)ntiles);                                                      \
+    else                                                                                                          \
+        hipLaunchKernelGGL((gemm_w8g32_tiles<TP, SCV, PKV>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, \
+                           ntiles, nullptr, (int64_t)0)
     switch (T_pad / 16 * 4 + scales) {
         case 4: W8I_TILES_LAUNCH(1, false, false); break;
         case 5: W8I_TILES_LAUNCH(1, true, false); break;
@@ -1232,6 +1293,20 @@ int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X
         return launch_tiles(Wp, Sp, X, t, T_pad, Y, N, K, ldx, ldy, 2, stream);
     const LinearPlan p = plan_packed(T_pad / 16, (N + kRows - 1) / kRows);
     return launch_split<kEpiStore, true>(p, Wp, Sp, X, t, Y, N, K, ldx, ldy, LinearEpilogue{nullptr, 0, 0}, stream);
+}
+
+int tiles_of(int64_t N) { return tile_count(N); }
+
+// the head projection on the persistent kernel with the max epilogue: y as w8_linear_invariant
+// (or _packed) gives it, and M [t][tiles_of(N)] the per-tile column maxima; T_pad <= 32 (or 48 / 64
+// with t <= 32)
+int launch_linear_max(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
+                      uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, float* M, hipStream_t stream) {
+    T_pad = kernel_width(t, T_pad);
+    if (T_pad > 32) return W8I_ET;
+    const bool s16 = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+    const int scales = packed ? 2 : ((K / kGroup) % 8 == 0 && s16 ? 1 : 0);
+    return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, scales, stream, M);
 }
 
 int launch_linear_pair(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,

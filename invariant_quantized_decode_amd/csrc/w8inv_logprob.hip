@@ -141,16 +141,18 @@ __device__ __forceinline__ float row_max_from_blocks(const float* M, int nb, int
     return m;
 }
 
+// M holds nm partial maxima per column (the nb block maxima, or the head
+// projection's per-tile maxima when it ran with the max epilogue).
 template <int E, bool VEC>
 __global__ __launch_bounds__(kLpThreads) void lp_block_sumexp(const uint16_t* __restrict__ L, int64_t V,
                                                               int64_t ldl, int nb, const float* __restrict__ M,
-                                                              float* __restrict__ P) {
+                                                              int nm, float* __restrict__ P) {
     constexpr int C = E < 8 ? E : 8;
     constexpr int NC = E / C;
     __shared__ float wsum[kLpThreads / 64];
     const int b = blockIdx.x, j = blockIdx.y;
     bool nan;
-    const float m = row_max_from_blocks<kLpThreads>(M, nb, j, nan);
+    const float m = row_max_from_blocks<kLpThreads>(M, nm, j, nan);
     if (nan) {
         if (threadIdx.x == 0) P[(int64_t)j * nb + b] = __builtin_nanf("");
         return;
@@ -197,13 +199,13 @@ constexpr int kFoldChunk = 1024;  // partials staged per pass
 template <bool DIRECT>
 __global__ __launch_bounds__(64) void lp_fold(const uint16_t* __restrict__ L, int64_t V, int64_t ldl,
                                                const int64_t* __restrict__ targets, int nb,
-                                               const float* __restrict__ M, const float* __restrict__ P,
+                                               const float* __restrict__ M, int nm, const float* __restrict__ P,
                                                float* __restrict__ out) {
     __shared__ __align__(16) float part[kFoldChunk];
     const int j = blockIdx.x;
     const int lane = threadIdx.x;
     bool nan;
-    const float m = row_max_from_blocks<64>(M, nb, j, nan);
+    const float m = row_max_from_blocks<64>(M, nm, j, nan);
     float S = 0.0f;
     for (int b0 = 0; b0 < nb; b0 += kFoldChunk) {
         const int n = nb - b0 < kFoldChunk ? nb - b0 : kFoldChunk;
@@ -247,19 +249,43 @@ size_t logprob_workspace_bytes(int t, int64_t V, int block) {
     return (size_t)(2 * round_up((int64_t)t * nb * (int64_t)sizeof(float), 256));
 }
 
+// with_max: the block-max pass first (M receives the nb block maxima); otherwise M already holds nm
+// partial maxima per column
 template <int E>
-static void launch_lp_e(const uint16_t* L, int64_t V, int64_t ldl, int nb, int t, float* M, float* P, bool vec,
-                        hipStream_t stream) {
+static void launch_lp_e(const uint16_t* L, int64_t V, int64_t ldl, int nb, int t, float* M, int nm, float* P,
+                        bool vec, bool with_max, hipStream_t stream) {
     const dim3 grid(nb, t), block(kLpThreads);
     if constexpr (E >= 8) {
         if (vec) {
-            hipLaunchKernelGGL((lp_block_max<E, true>), grid, block, 0, stream, L, V, ldl, nb, M);
-            hipLaunchKernelGGL((lp_block_sumexp<E, true>), grid, block, 0, stream, L, V, ldl, nb, M, P);
+            if (with_max) hipLaunchKernelGGL((lp_block_max<E, true>), grid, block, 0, stream, L, V, ldl, nb, M);
+            hipLaunchKernelGGL((lp_block_sumexp<E, true>), grid, block, 0, stream, L, V, ldl, nb, M, nm, P);
             return;
         }
     }
-    hipLaunchKernelGGL((lp_block_max<E, false>), grid, block, 0, stream, L, V, ldl, nb, M);
-    hipLaunchKernelGGL((lp_block_sumexp<E, false>), grid, block, 0, stream, L, V, ldl, nb, M, P);
+    if (with_max) hipLaunchKernelGGL((lp_block_max<E, false>), grid, block, 0, stream, L, V, ldl, nb, M);
+    hipLaunchKernelGGL((lp_block_sumexp<E, false>), grid, block, 0, stream, L, V, ldl, nb, M, nm, P);
+}
+
+static int launch_lp(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V, int64_t ldl,
+                     float* M, int nm, float* P, bool with_max, bool direct, hipStream_t stream) {
+    const int nb = (int)((V + block - 1) / block);
+    const bool vec = (reinterpret_cast<uintptr_t>(L) % 16 == 0) && (ldl % 8 == 0);
+    switch (block / kLpThreads) {
+        case 1: launch_lp_e<1>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 2: launch_lp_e<2>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 4: launch_lp_e<4>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 8: launch_lp_e<8>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 16: launch_lp_e<16>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 32: launch_lp_e<32>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 64: launch_lp_e<64>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        case 128: launch_lp_e<128>(L, V, ldl, nb, t, M, nm, P, vec, with_max, stream); break;
+        default: return W8I_EBLOCK;
+    }
+    if (direct)
+        hipLaunchKernelGGL(lp_fold<true>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, nb, M, nm, P, out);
+    else
+        hipLaunchKernelGGL(lp_fold<false>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, nb, M, nm, P, out);
+    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
 }
 
 int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V, int64_t ldl,
@@ -268,23 +294,20 @@ int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* 
     float* M = static_cast<float*>(ws);
     float* P = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                         round_up((int64_t)t * nb * (int64_t)sizeof(float), 256));
-    const bool vec = (reinterpret_cast<uintptr_t>(L) % 16 == 0) && (ldl % 8 == 0);
-    switch (block / kLpThreads) {
-        case 1: launch_lp_e<1>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 2: launch_lp_e<2>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 4: launch_lp_e<4>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 8: launch_lp_e<8>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 16: launch_lp_e<16>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 32: launch_lp_e<32>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 64: launch_lp_e<64>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        case 128: launch_lp_e<128>(L, V, ldl, (int)nb, t, M, P, vec, stream); break;
-        default: return W8I_EBLOCK;
-    }
-    if (direct)
-        hipLaunchKernelGGL(lp_fold<true>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
-    else
-        hipLaunchKernelGGL(lp_fold<false>, dim3(t), dim3(64), 0, stream, L, V, ldl, targets, (int)nb, M, P, out);
-    return hipGetLastError() == hipSuccess ? W8I_OK : W8I_EHIP;
+    return launch_lp(L, targets, block, out, t, V, ldl, M, (int)nb, P, true, direct, stream);
+}
+
+size_t logprob_from_max_workspace_bytes(int t, int64_t V, int block, int nm) {
+    const int64_t nb = (V + block - 1) / block;
+    return (size_t)(round_up((int64_t)t * nm * (int64_t)sizeof(float), 256) +
+                    round_up((int64_t)t * nb * (int64_t)sizeof(float), 256));
+}
+
+int launch_logprob_from_max(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,
+                            int64_t ldl, void* ws, int nm, hipStream_t stream) {
+    float* M = static_cast<float*>(ws);
+    float* P = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((int64_t)t * nm * (int64_t)sizeof(float), 256));
+    return launch_lp(L, targets, block, out, t, V, ldl, M, nm, P, false, false, stream);
 }
 
 // ------------------------------------------- scratch of the no-alloc entry point

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 29
+    assert len(names) == 32
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -224,6 +224,24 @@ def test_pair_and_attn_input_proj_validation():
     assert g(*args(h=None)) == -1 and g(*args(H=70000, ldh=70000)) == -2 and g(*args(ldh=100)) == -2
     assert g(*args(H=5100, ldh=5100)) == -2           # the projection's K = H must be a multiple of 32
     assert g(*args(T=40)) == -4 and g(*args(W=None)) == -1
+
+
+def test_fused_head_logprob_validation():
+    f = L.w8_head_logprob_invariant
+    need = L.w8_head_logprob_workspace_bytes(32, 248320, 4096)
+    assert need == 32 * 970 * 4 + 32 * 61 * 4 + (256 - 32 * 61 * 4 % 256)  # maxima and partials, each 256-aligned
+    assert L.w8_head_logprob_workspace_bytes(32, 248320, 1000) == 0
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(  # noqa: E731
+        W=fake(A), S=fake(A), x=fake(A), tg=fake(A), t=4, T=32, block=4096, lg=fake(A), out=fake(A), V=248320,
+        K=5120, ldx=5120, ldl=248320, ws=fake(A), wsb=L.w8_head_logprob_workspace_bytes(4, 248320, 4096),
+        st=None).items()]
+    need = L.w8_head_logprob_workspace_bytes(4, 248320, 4096)
+    assert f(*args(t=0, W=None)) == 0
+    assert f(*args(T=64, t=40)) == -4 and f(*args(T=24)) == -4
+    assert f(*args(block=1000)) == -5 and f(*args(tg=None)) == -1 and f(*args(out=None)) == -1
+    assert f(*args(ldl=1000)) == -2 and f(*args(ws=None)) == -6 and f(*args(wsb=need - 4)) == -6
+    assert f(*args(ws=fake(A + 8))) == -3 and f(*args(out=fake(A + 2))) == -3
+    assert L.w8_head_logprob_invariant_packed(*args(S=fake(A + 2))) == -3
 
 
 def test_glue_and_hooks_reject_invalid_arguments():
