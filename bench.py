@@ -18,7 +18,7 @@ their own, the same way, for the roofline.  The 6144x5120 projection at T_pad 32
 sub-record.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1] [--all [--only TEXT]]
-                  [--pmc-pass {head,linear6144}]
+                  [--pmc-pass {head,linear6144,mlp_gate_up}]
 """
 from __future__ import annotations
 
@@ -55,7 +55,7 @@ def parse():
                         "the chain's, at t=1 and t=T_pad, and the head's logprob), with the CPU oracle on a row sample")
     p.add_argument("--only", default="",
                    help="with --all: only the workloads whose name contains this text")
-    p.add_argument("--pmc-pass", choices=("head", "linear6144"), default=None,
+    p.add_argument("--pmc-pass", choices=("head", "linear6144", "mlp_gate_up"), default=None,
                    help="for rocprofv3 --pmc: 3 launches of the workload's projection kernel at t=T_pad and 3 at "
                         "t=1, then a plain 512 MiB device copy 3 times (the calibration for the HBM byte "
                         "counters); prints one short JSON line")
@@ -528,7 +528,7 @@ def cpu_baseline(torch, q, s, pool, targets, block, base_logits, base_lp, wbytes
 def pmc_pass(torch, w8, synth, dev, which: str):
     """For rocprofv3 --pmc runs: 3 launches of the workload's projection kernel (packed layout) at
     t = T_pad and 3 at t = 1, then a plain 512 MiB device copy 3 times (the counters' calibration)."""
-    case = synth.HEAD if which == "head" else synth.LINEAR_6144
+    case = {"head": synth.HEAD, "linear6144": synth.LINEAR_6144, "mlp_gate_up": synth.MLP_GATE_UP}[which]
     N, K, T_pad = case.N, case.K, case.T_pad
     rng = np.random.default_rng(case.seed)
     q = synth.draw_codes(rng, N, K)

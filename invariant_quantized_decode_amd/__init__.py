@@ -42,10 +42,11 @@ class W8InvError(ValueError):
         super().__init__(f"{fn} returned {status} ({_lib.w8i_status_string(status).decode()})")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
-    L = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH):
+    """Open a build of the library at `path` and declare the C signatures of its entry points."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(path)
     P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     L.w8i_status_string.argtypes, L.w8i_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.w8i_version.argtypes, L.w8i_version.restype = [], ctypes.c_char_p

@@ -32,14 +32,22 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+def compile_source(path: str, obj: str, include_dir: str = CSRC) -> str:
+    """hipcc -c of one source with the library's flags (`include_dir` holds its private headers)."""
+    flags = [f if f != CSRC else include_dir for f in FLAGS]
+    r = subprocess.run([HIPCC, *flags, "-c", path, "-o", obj], capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed on {src}")
+        raise RuntimeError(f"hipcc failed on {path}")
     return obj
+
+
+def _compile(src: str) -> str:
+    return compile_source(os.path.join(CSRC, src), os.path.join(BUILD, src.replace(".hip", ".o")))
+
+
+def link_objects(objs: list, lib: str) -> None:
+    _link(objs, lib)
 
 
 def _link(objs: list, lib: str) -> None:

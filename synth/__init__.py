@@ -195,3 +195,34 @@ def random_logits(seed: int, t: int, V: int, std: float = 105.0):
     l = f32_to_bf16_bits((rng.standard_normal(size=(t, V), dtype=np.float32) * np.float32(std)))
     tg = rng.integers(0, V, size=t, dtype=np.int64)
     return l, tg
+
+
+def order_sensitive_linear(seed: int, N: int, K: int, t: int):
+    """A projection problem whose result depends on the order of its fp64 sums.
+
+    Every 32-group of a weight row has at most one nonzero code, so each group's dot product is a
+    single exact product.  Each row holds a pair of codes +100 / -100, both with scale 1024, at two
+    distinct random groups; their positions see activations of 2^40 (offset 0 of every group), so
+    the pair's terms are +-100 * 1024 * 2^40 and cancel exactly.  Every other group contributes one
+    term of order 10^2 (a code at offset 1, scale |N(0, 1)| + 0.01, activation N(0, 1)), which a
+    running sum that holds one term of the pair keeps only to a multiple of 16.  Which of those terms
+    are added while the pair is half summed depends on the order of the additions, so different
+    orders give different bf16 results for most rows.
+    """
+    rng = np.random.default_rng(seed)
+    G = K // GROUP
+    q = np.zeros((N, K), dtype=np.int8)
+    q[:, 1::GROUP] = rng.integers(-127, 128, size=(N, G), dtype=np.int8)
+    s = f64_to_f16_bits(np.abs(rng.normal(0.0, 1.0, size=(N, G))) + 0.01)
+    a = rng.integers(0, G, size=N)
+    b = rng.integers(0, G - 1, size=N)
+    b = b + (b >= a)
+    r = np.arange(N)
+    q[r, GROUP * a + 1] = 0
+    q[r, GROUP * b + 1] = 0
+    q[r, GROUP * a] = 100
+    q[r, GROUP * b] = -100
+    s[r, a] = s[r, b] = f64_to_f16_bits(np.array(1024.0))
+    x = f32_to_bf16_bits(rng.standard_normal(size=(t, K), dtype=np.float32))
+    x[:, 0::GROUP] = f32_to_bf16_bits(np.full((t, G), 2.0 ** 40, dtype=np.float32))
+    return q, s, x
