@@ -588,6 +588,10 @@ def run_all(torch, w8, synth, dev, args):
     work += [(n, N, K, synth.CHAIN_T_PAD, 0.0, "linear") for n, N, K in chain]
     # the same projections over the packed layout (w8_pack, prepared once per weight copy)
     work += [(n, N, K, T, e, "packed") for n, N, K, T, e, _ in list(work)]
+    # where a workspace lets small N run the K-slice kernels and their fold launch, that path beside
+    # the default one-launch kernel
+    work += [(n, N, K, T, e, op + "_ks") for n, N, K, T, e, op in list(work)
+             if w8.w8_linear_invariant_workspace_bytes(N, K, T) > 0]
     # the chain's projections with their glue fused into the epilogue
     work += [("chain o + residual (fused) 5120x6144", 5120, 6144, synth.CHAIN_T_PAD, 0.0, "add"),
              ("chain gate+up + SwiGLU (fused) 34816x5120", 34816, 5120, synth.CHAIN_T_PAD, 0.0, "swiglu"),
@@ -599,8 +603,11 @@ def run_all(torch, w8, synth, dev, args):
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     stream = torch.cuda.Stream(device=dev)
+    def label(name: str, op: str) -> str:
+        return name + (" [packed]" if "packed" in op else "") + (" [K-slice + fold]" if op.endswith("_ks") else "")
+
     for name, N, K, T_pad, eps, op in work:
-        if not want(name + (" [packed]" if op.endswith("packed") else "")):
+        if not want(label(name, op)):
             continue
         wbytes = N * K + 2 * N * (K // 32)
         copies = max(1, math.ceil((1 << 30) / wbytes))
@@ -609,7 +616,7 @@ def run_all(torch, w8, synth, dev, args):
         X = torch.randn(T_pad, K, generator=g, device=dev).to(torch.bfloat16)
         R = torch.randn(T_pad, N, generator=g, device=dev).to(torch.bfloat16)
         Y = torch.empty((T_pad, N // 2 if op.startswith("swiglu") else N), dtype=torch.bfloat16, device=dev)
-        if op.endswith("packed"):
+        if op.endswith("packed") or op == "packed_ks":
             Ps = [w8.w8_pack(Ws[i], Ss[i]) for i in range(copies)]
         # the width the kernels run at: T_pad 48 / 64 calls with t <= 32 run the T_pad 32 kernel
         width = lambda t: T_pad if T_pad <= 32 or t > 32 else 32  # noqa: E731
@@ -619,6 +626,13 @@ def run_all(torch, w8, synth, dev, args):
         elif op == "packed":
             kernel = lambda t: w8.w8_linear_invariant_packed_kernel(N, K, width(t))  # noqa: E731
             call = lambda i, t: w8.w8_linear_invariant_packed(Ps[i][0], Ps[i][1], X[:t], t, T_pad, N, y=Y)  # noqa
+        elif op == "linear_ks":
+            kernel = lambda t: f"gemm_w8g32_kslice<{width(t) // 16}, false> + kslice_fold"  # noqa: E731
+            call = lambda i, t: w8.w8_linear_invariant(Ws[i], Ss[i], X[:t], t, T_pad, y=Y, workspace="auto")  # noqa
+        elif op == "packed_ks":
+            kernel = lambda t: f"gemm_w8g32_kslice<{width(t) // 16}, true> + kslice_fold"  # noqa: E731
+            call = lambda i, t: w8.w8_linear_invariant_packed(Ps[i][0], Ps[i][1], X[:t], t, T_pad, N, y=Y,  # noqa
+                                                              workspace="auto")
         elif op == "add":
             kernel = "gemm_w8g32_split_lds, residual-add epilogue"
             call = lambda i, t: w8.w8_linear_add_invariant(Ws[i], Ss[i], X[:t], R[:t], t, T_pad, y=Y)  # noqa: E731
@@ -662,7 +676,7 @@ def run_all(torch, w8, synth, dev, args):
             c0 = time.perf_counter()
             oracle.w8_linear(qh, sh, xh)
             csec = time.perf_counter() - c0
-            print(json.dumps({"workload": name + (" [packed]" if op.endswith("packed") else ""), "kernel": kernel(t) if callable(kernel) else kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
+            print(json.dumps({"workload": label(name, op), "kernel": kernel(t) if callable(kernel) else kernel, "t": t, "T_pad": T_pad, "us": round(sec * 1e6, 2),
                               "weight_gbs": round(wbytes / sec / 1e9, 1),
                               "roofline_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
                               "tflops_useful": round(2.0 * N * K * t / sec / 1e12, 3),

@@ -101,8 +101,17 @@ const char *w8i_version(void);
  *   being padding only.  Every live column's MFMAs, fp64 sums and rounding are
  *   the same for every t and every T_pad.
  *
- * workspace: this kernel needs none; the size query returns 0 and workspace
- * may be NULL.
+ * workspace (optional, never required; caller-owned device memory, 8-byte
+ * aligned, not overlapping the other buffers): the size query returns 0 where
+ * the call cannot use one, and for small N (at most 2048 rows, run at T_pad 16
+ * or 32) the bytes of 8 fp64 slice sums per output, 8 * min(T_pad, 32) * N *
+ * 8.  Given a workspace of at least 8 * t * N * 8 bytes such a call runs the 8
+ * K-slices of each 32-row strip on separate workgroups (gemm_w8g32_kslice),
+ * parks each slice sum in the workspace and folds them in a second launch
+ * (kslice_fold): the same slices, MFMAs, fp64 operations in the same order,
+ * left fold and rounding, so the same bits as the one-launch kernel, which
+ * runs when workspace is NULL or smaller.  The workspace's contents on return
+ * are unspecified.  W8I_EALIGN if a non-NULL workspace is not 8-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t w8_linear_invariant_workspace_bytes(int64_t N, int64_t K, int32_t T_pad);
 
@@ -116,7 +125,9 @@ int w8_linear_invariant(const int8_t *W_q, const uint16_t *scales, const uint16_
  * The choice depends on N, K, T_pad and on whether `scales` is 16-byte
  * aligned, and every kernel runs the K plan above, so it changes no bit of the
  * result.  t enters only at T_pad 48 or 64: a call with t <= 32 runs the kernel
- * this query names for T_pad 32.  Pure host function: no device access. */
+ * this query names for T_pad 32.  The name is that of the one-launch kernel; a
+ * call given the optional workspace (below) runs gemm_w8g32_kslice and
+ * kslice_fold instead.  Pure host function: no device access. */
 const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t *scales);
 
 /* ---------------------------------------------------------------------------
@@ -143,23 +154,30 @@ const char *w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, cons
  *   from W_q (16-byte aligned) and scales (2-byte aligned) on `stream`; no
  *   overlap between the inputs and the outputs.
  * w8_linear_invariant_packed: as w8_linear_invariant (x, y, t, T_pad, N, K,
- *   ldx, ldy and their rules), with Wp / Sp from w8_pack(N, K) (16-byte
- *   aligned).  No workspace.  Any N: the persistent kernel where the plain
- *   layout runs it (T_pad <= 32, N >= 131072), else the LDS-staged split
- *   kernel, both with per-stage scale loads.
+ *   ldx, ldy, workspace and their rules), with Wp / Sp from w8_pack(N, K)
+ *   (16-byte aligned).  Any N: the persistent kernel where the plain layout
+ *   runs it (T_pad <= 32, N >= 131072), the K-slice kernels for small N given
+ *   the workspace, else the LDS-staged split kernel, all with per-stage scale
+ *   loads.
+ * w8_linear_invariant_packed_workspace_bytes: the workspace size query, equal
+ *   to w8_linear_invariant_workspace_bytes for the same (N, K, T_pad).
  * ------------------------------------------------------------------------- */
 int w8_pack_bytes(int64_t N, int64_t K, size_t *wp_bytes, size_t *sp_bytes);
 
 int w8_pack(const int8_t *W_q, const uint16_t *scales, int64_t N, int64_t K, int8_t *Wp, uint16_t *Sp,
             void *stream);
 
+size_t w8_linear_invariant_packed_workspace_bytes(int64_t N, int64_t K, int32_t T_pad);
+
 int w8_linear_invariant_packed(const int8_t *Wp, const uint16_t *Sp, const uint16_t *x, int32_t t,
                                int32_t T_pad, uint16_t *y, int64_t N, int64_t K, int64_t ldx, int64_t ldy,
-                               void *stream);
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Name of the kernel w8_linear_invariant_packed runs (static storage; "" for
  * arguments it would reject): a function of N and T_pad (at T_pad 48 or 64 a
- * call with t <= 32 runs the kernel named for T_pad 32).  Pure host function. */
+ * call with t <= 32 runs the kernel named for T_pad 32; given the optional
+ * workspace, small N runs the K-slice kernel and its fold instead).  Pure
+ * host function. */
 const char *w8_linear_invariant_packed_kernel(int64_t N, int64_t K, int32_t T_pad);
 
 /* ---------------------------------------------------------------------------

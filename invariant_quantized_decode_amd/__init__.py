@@ -33,7 +33,8 @@ EXPORTS = ("w8i_status_string", "w8i_version", "w8_linear_invariant_workspace_by
            "w8i_residual_add", "w8i_exp32", "w8i_log32", "vocab_block_logprob_noalloc",
            "w8_linear_pair_invariant", "w8_linear_pair_invariant_packed", "w8_attn_input_proj_workspace_bytes",
            "w8_attn_input_proj_invariant", "w8_attn_input_proj_invariant_packed", "w8_head_logprob_workspace_bytes",
-           "w8_head_logprob_invariant", "w8_head_logprob_invariant_packed")
+           "w8_head_logprob_invariant", "w8_head_logprob_invariant_packed",
+           "w8_linear_invariant_packed_workspace_bytes")
 
 
 class W8InvError(ValueError):
@@ -59,7 +60,9 @@ def _load(path: str = LIB_PATH):
     L.w8_linear_swiglu_invariant.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
     L.w8_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
     L.w8_pack.argtypes = [P, P, I64, I64, P, P, P]
-    L.w8_linear_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
+    L.w8_linear_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P, SZ, P]
+    L.w8_linear_invariant_packed_workspace_bytes.argtypes = [I64, I64, I32]
+    L.w8_linear_invariant_packed_workspace_bytes.restype = SZ
     L.w8_linear_add_invariant_packed.argtypes = [P, P, P, P, I32, I32, P, I64, I64, I64, I64, I64, P]
     L.w8_linear_swiglu_invariant_packed.argtypes = [P, P, P, I32, I32, P, I64, I64, I64, I64, P]
     L.w8_linear_invariant_packed_kernel.argtypes = [I64, I64, I32]
@@ -172,15 +175,42 @@ def _projection_args(W_q, scales, x, t, y, y_cols):
     return N, K, ldx, y, ldy
 
 
+def _projection_workspace(workspace, need: int, device):
+    """The optional workspace of a projection: None passes none (the one-launch kernel runs), "auto"
+    allocates the queried size (none if it is 0; small N then runs its K-slices on separate workgroups
+    and a fold launch), a contiguous uint8 tensor is used as given."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 tensor')
+        return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return workspace
+
+
+def w8_linear_invariant_workspace_bytes(N: int, K: int, T_pad: int) -> int:
+    return int(_lib.w8_linear_invariant_workspace_bytes(int(N), int(K), int(T_pad)))
+
+
+def w8_linear_invariant_packed_workspace_bytes(N: int, K: int, T_pad: int) -> int:
+    return int(_lib.w8_linear_invariant_packed_workspace_bytes(int(N), int(K), int(T_pad)))
+
+
 def w8_linear_invariant(W_q: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, t: int, T_pad: int,
-                        y: torch.Tensor | None = None) -> torch.Tensor:
+                        y: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
     """y[:t] = bf16(dequant(W_q, scales) @ x[:t]^T) at the fixed width T_pad.
 
     W_q int8 [N, K]; scales fp16 [N, K/32]; x bf16 [>=t, K] (token rows); y bf16 [t, N] (allocated if None).
+    workspace: None (the one-launch kernel), "auto" (the size w8_linear_invariant_workspace_bytes asks for;
+    small N then runs its K-slices on separate workgroups and a fold launch), or a uint8 tensor.  The bits
+    do not depend on it.
     """
     N, K, ldx, y, ldy = _projection_args(W_q, scales, x, t, y, W_q.shape[0])
+    ws = _projection_workspace(workspace, w8_linear_invariant_workspace_bytes(N, K, T_pad), W_q.device)
+    if ws is not None:
+        _same_gpu(("W_q", W_q), ("workspace", ws))
     st = _launch(_lib.w8_linear_invariant, W_q.device, _ptr(W_q), _ptr(scales), _ptr(x), int(t), int(T_pad), _ptr(y),
-                 N, K, ldx, ldy, None, 0)
+                 N, K, ldx, ldy, _ptr(ws), ws.numel() if ws is not None else 0)
     _check("w8_linear_invariant", st)
     return y
 
@@ -253,11 +283,15 @@ def _packed_args(Wp, Sp, x, t, N, rows, y, y_cols):
 
 
 def w8_linear_invariant_packed(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, t: int, T_pad: int, N: int,
-                               y: torch.Tensor | None = None) -> torch.Tensor:
-    """w8_linear_invariant over the packed layout from w8_pack (same bits).  x bf16 [>=t, K]; y bf16 [t, N]."""
+                               y: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
+    """w8_linear_invariant over the packed layout from w8_pack (same bits).  x bf16 [>=t, K]; y bf16 [t, N];
+    workspace as for w8_linear_invariant."""
     K, y = _packed_args(Wp, Sp, x, t, N, N, y, N)
+    ws = _projection_workspace(workspace, w8_linear_invariant_packed_workspace_bytes(N, K, T_pad), Wp.device)
+    if ws is not None:
+        _same_gpu(("Wp", Wp), ("workspace", ws))
     st = _launch(_lib.w8_linear_invariant_packed, Wp.device, _ptr(Wp), _ptr(Sp), _ptr(x), int(t), int(T_pad), _ptr(y),
-                 int(N), K, _row_major(x, "x"), _row_major(y, "y"))
+                 int(N), K, _row_major(x, "x"), _row_major(y, "y"), _ptr(ws), ws.numel() if ws is not None else 0)
     _check("w8_linear_invariant_packed", st)
     return y
 
@@ -629,7 +663,7 @@ def kernel_source_digest() -> str:
     kernel a stored counter profile measured."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("w8inv_gemm.hip", "w8inv_math.h", "w8inv_internal.h"):
+    for name in ("w8inv_gemm.hip", "w8inv_gemm_common.h", "w8inv_math.h", "w8inv_internal.h"):
         with open(os.path.join(_HERE, "csrc", name), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]

@@ -17,7 +17,7 @@ CALIB_LIB = os.path.join(PKG, "libw8calib.so")
 CALIB_SOURCES = ["w8calib.hip"]
 
 SOURCES = ["w8inv_api.hip", "w8inv_gemm.hip", "w8inv_logprob.hip", "w8inv_glue.hip", "w8inv_pack.hip",
-           "w8inv_argmax.hip"]
+           "w8inv_argmax.hip", "w8inv_kslice.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -56,20 +56,19 @@ const char* w8i_status_string(int status) {
 const char* w8i_version(void) { return "w8inv 0.1 (gfx950)"; }
 
 size_t w8_linear_invariant_workspace_bytes(int64_t N, int64_t K, int32_t T_pad) {
-    (void)N;
-    (void)K;
-    (void)T_pad;
-    return 0;
+    if (N < 1 || K < kGroup || K % kGroup != 0 || N > kMaxDim || K > kMaxDim) return 0;
+    if (T_pad != 16 && T_pad != 32 && T_pad != 48 && T_pad != 64) return 0;
+    return kslice_workspace_bytes(N, T_pad);
 }
 
 int w8_linear_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, int32_t t, int32_t T_pad,
                         uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* workspace,
                         size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     const int st = check_projection(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, N);
     if (st != W8I_OK || t == 0) return st;
-    return launch_linear(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
+    if (workspace && !aligned(workspace, 8)) return W8I_EALIGN;
+    return launch_linear(W_q, scales, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream), workspace,
+                         workspace_bytes);
 }
 
 const char* w8_linear_invariant_kernel(int64_t N, int64_t K, int32_t T_pad, const uint16_t* scales) {
@@ -94,13 +93,20 @@ int w8_pack(const int8_t* W_q, const uint16_t* scales, int64_t N, int64_t K, int
     return launch_pack(W_q, scales, N, K, Wp, Sp, as_stream(stream));
 }
 
+size_t w8_linear_invariant_packed_workspace_bytes(int64_t N, int64_t K, int32_t T_pad) {
+    return w8_linear_invariant_workspace_bytes(N, K, T_pad);
+}
+
 int w8_linear_invariant_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* x, int32_t t, int32_t T_pad,
-                               uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* stream) {
+                               uint16_t* y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     const int st = check_projection(Wp, Sp, x, t, T_pad, y, N, K, ldx, ldy, N);
     if (st != W8I_OK || t == 0) return st;
     if (packed_weight_bytes(N, K) >= ((int64_t)1 << 32)) return W8I_ESHAPE;
     if (!aligned(Sp, 16)) return W8I_EALIGN;
-    return launch_linear_packed(Wp, Sp, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream));
+    if (workspace && !aligned(workspace, 8)) return W8I_EALIGN;
+    return launch_linear_packed(Wp, Sp, x, t, T_pad, y, N, K, ldx, ldy, as_stream(stream), workspace,
+                                workspace_bytes);
 }
 
 const char* w8_linear_invariant_packed_kernel(int64_t N, int64_t K, int32_t T_pad) {

@@ -46,11 +46,21 @@ struct LinearEpilogue {
     int wg1 = 0;
 };
 
+// ws: the caller's workspace (may be null); with at least kKSlices * t * N doubles
+// and a small N (kslice_applies) the K-slice kernels run, with the same bits
 int launch_linear(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
-                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream, void* ws = nullptr,
+                  size_t ws_bytes = 0);
 // the projection over weights and scales in the packed layout (w8_pack)
 int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X, int t, int T_pad, uint16_t* Y,
-                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream);
+                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, hipStream_t stream, void* ws = nullptr,
+                         size_t ws_bytes = 0);
+// Small N (w8inv_kslice.hip): the 8 K-slices of each strip on separate workgroups, their fp64
+// sums in a workspace [8][t][N], then the left fold; T_pad is the width the kernels run at.
+bool kslice_applies(int64_t N, int T_pad);
+size_t kslice_workspace_bytes(int64_t N, int T_pad);  // 0 where the K-slice kernels do not run
+int launch_kslice(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
+                  int64_t N, int64_t K, int64_t ldx, int64_t ldy, void* ws, hipStream_t stream);
 // bytes of the packed layout of an [N, K] projection: 32-row strips x ceil(K/64) blocks
 inline int64_t packed_weight_bytes(int64_t N, int64_t K) { return (N + 31) / 32 * ((K / kGroup + 1) / 2) * 2048; }
 inline int64_t packed_scale_bytes(int64_t N, int64_t K) { return (N + 31) / 32 * ((K / kGroup + 1) / 2) * 128; }

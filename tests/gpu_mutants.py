@@ -1,8 +1,9 @@
 """Mutated builds of the HIP library, for the GPU mutant tier (tests/test_gpu_mutants.py).
 
 TEST INFRASTRUCTURE ONLY.  Each mutant plants one plausible mistake in a copy of one translation unit
-of the library -- a reduction schedule chosen from t, a reordered fold, a local instead of a global
-shift, a different in-block tree -- and is linked with the product's other objects into
+of the library -- a reduction schedule chosen from t, a reordered fold (of the slice sums, in one launch
+or in the small-N fold launch, or of the logprob's block partials), a local instead of a global shift, a
+different in-block tree -- and is linked with the product's other objects into
 tests/mutant_libs/lib_<name>.so.  The GPU tests load each one beside the product library and check
 that their invariance and parity checks catch it while the product passes them.  Every mutation keeps
 all memory accesses and loop bounds of the code it replaces (no mutant can fault or hang).  The
@@ -44,6 +45,12 @@ MUTANTS = {
         ("        double sum = *part(0, V);\n#pragma unroll\n        for (int w = 1; w < kKSlices; ++w) sum = sum + *part(w, V);",
          "        double sum = *part(t > 16 ? kKSlices - 1 : 0, V);\n#pragma unroll\n"
          "        for (int w = 1; w < kKSlices; ++w) sum = sum + *part(t > 16 ? kKSlices - 1 - w : w, V);"),
+    ]),
+    # the K-slice path's fold launch folds the 8 slice sums from the last when t > 16
+    "kslice_fold_reversed_from_t": ("w8inv_kslice.hip", [
+        ("    double sum = p[0];\n#pragma unroll\n    for (int w = 1; w < kKSlices; ++w) sum = sum + p[w * stride];",
+         "    double sum = p[t > 16 ? (kKSlices - 1) * stride : 0];\n#pragma unroll\n"
+         "    for (int w = 1; w < kKSlices; ++w) sum = sum + p[(t > 16 ? kKSlices - 1 - w : w) * stride];"),
     ]),
     # the logprob's fold adds four block partials together before adding them to the running sum
     "block_fold_regrouped": ("w8inv_logprob.hip", [

@@ -39,29 +39,31 @@ class OrderSensitiveProjection:
             np.concatenate([np.arange(64), rng.choice(N, model_rows - 128, replace=False), np.arange(N - 64, N)]))
         self.want = order_model.documented_schedule(q, s, x, self.rows)
 
-    def call(self, packed: bool, xd, t: int):
+    def call(self, packed: bool, xd, t: int, workspace="auto"):
         if packed:
-            return w8.w8_linear_invariant_packed(self.Wp, self.Sp, xd, t, self.T_pad, self.N)
-        return w8.w8_linear_invariant(self.W, self.S, xd, t, self.T_pad)
+            return w8.w8_linear_invariant_packed(self.Wp, self.Sp, xd, t, self.T_pad, self.N, workspace=workspace)
+        return w8.w8_linear_invariant(self.W, self.S, xd, t, self.T_pad, workspace=workspace)
 
 
 def check_projection(P: OrderSensitiveProjection) -> list:
     """The t = T_pad call gives the documented schedule's bits on the model rows, and every column
     computed at t < T_pad (a random subset of the columns, in random order) gives its t = T_pad bits;
-    both weight layouts."""
+    both weight layouts, with the workspace the size query asks for (small N: the K-slice kernels) and
+    without one (the one-launch kernels)."""
     fails = []
     for packed in (False, True):
-        tag = f"{P.name} {'packed' if packed else 'plain'}"
-        full = bits(P.call(packed, P.X, P.T_pad))
-        bad = int(np.sum(full[:, P.rows] != P.want))
-        if bad:
-            fails.append(f"{tag}: t={P.T_pad} differs from the documented schedule in {bad} of {P.want.size}")
-        rng = np.random.default_rng(P.seed + 1)
-        for t in (t for t in INVARIANCE_T if t < P.T_pad):
-            perm = rng.permutation(P.T_pad)[:t]
-            bad = int(np.sum(bits(P.call(packed, bf16(P.x[perm]), t)) != full[perm]))
+        for ws in ("auto", None):
+            tag = f"{P.name} {'packed' if packed else 'plain'}{'' if ws else ' no workspace'}"
+            full = bits(P.call(packed, P.X, P.T_pad, ws))
+            bad = int(np.sum(full[:, P.rows] != P.want))
             if bad:
-                fails.append(f"{tag}: t={t} columns differ from their t={P.T_pad} bits in {bad} of {t * P.N}")
+                fails.append(f"{tag}: t={P.T_pad} differs from the documented schedule in {bad} of {P.want.size}")
+            rng = np.random.default_rng(P.seed + 1)
+            for t in (t for t in INVARIANCE_T if t < P.T_pad):
+                perm = rng.permutation(P.T_pad)[:t]
+                bad = int(np.sum(bits(P.call(packed, bf16(P.x[perm]), t, ws)) != full[perm]))
+                if bad:
+                    fails.append(f"{tag}: t={t} columns differ from their t={P.T_pad} bits in {bad} of {t * P.N}")
     return fails
 
 

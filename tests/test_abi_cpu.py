@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 32
+    assert len(names) == 33
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(w8.EXPORTS)
@@ -73,7 +73,26 @@ def test_linear_rejects_invalid_arguments(kw, code):
 
 def test_linear_t_zero_is_a_no_op():
     assert linear(t=0, W=0, S=0, X=0, Y=0) == 0
-    assert L.w8_linear_invariant_workspace_bytes(6144, 5120, 32) == 0
+
+
+def test_workspace_queries():
+    """The K-slice workspace: 8 fp64 sums per output at the width the kernels run at (min(T_pad, 32)),
+    for at most 64 strips of 32 rows; 0 elsewhere and for arguments a call would reject."""
+    for q in (L.w8_linear_invariant_workspace_bytes, L.w8_linear_invariant_packed_workspace_bytes):
+        q.restype = ctypes.c_size_t
+        assert q(6144, 5120, 32) == 0                      # 192 strips: the one-launch kernels
+        assert q(1024, 5120, 16) == 8 * 16 * 1024 * 8
+        assert q(1024, 5120, 32) == 8 * 32 * 1024 * 8
+        assert q(1000, 5120, 64) == 8 * 32 * 1000 * 8       # run at 32 when t <= 32
+        assert q(2048, 1024, 48) == 8 * 32 * 2048 * 8
+        assert q(2049, 1024, 32) == 0                       # 65 strips
+        assert q(1024, 5100, 32) == 0 and q(1024, 5120, 24) == 0 and q(0, 5120, 32) == 0
+
+
+def test_misaligned_workspace_is_rejected():
+    args = (fake(A), fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 64)
+    assert L.w8_linear_invariant(*args, fake(A + 4), 1 << 20, None) == -3
+    assert L.w8_linear_invariant_packed(*args, fake(A + 4), 1 << 20, None) == -3
 
 
 def linear_add(W=A, S=A, X=A, R=A + 0x100000, t=4, T=32, Y=A + 0x200000, N=64, K=256, ldx=256, ldr=64, ldy=64):
@@ -127,6 +146,7 @@ def test_pack_sizes_and_validation():
 def test_packed_kernel_query():
     q = L.w8_linear_invariant_packed_kernel
     assert q(6144, 5120, 32) == b"gemm_w8g32_split_lds<2, 3, false, 0, true>"
+    assert q(1024, 5120, 64) == b"gemm_w8g32_split_lds<4, 2, false, 0, true>"  # t > 32 at T_pad 64
     assert q(34816, 5120, 64) == b"gemm_w8g32_split_lds<4, 2, false, 0, true>"
     assert q(248320, 5120, 32) == b"gemm_w8g32_tiles<2, false, true>"
     assert q(248320, 5120, 64) == b"gemm_w8g32_split_lds<4, 2, false, 0, true>"
@@ -135,11 +155,11 @@ def test_packed_kernel_query():
 
 def test_packed_linear_validation():
     f = L.w8_linear_invariant_packed
-    assert f(fake(A), fake(A), fake(A), 0, 32, fake(A), 64, 256, 256, 64, None) == 0
-    assert f(fake(A), fake(A), fake(A), 4, 24, fake(A), 64, 256, 256, 64, None) == -4
-    assert f(fake(A), fake(A + 4), fake(A), 4, 32, fake(A), 64, 256, 256, 64, None) == -3
-    assert f(None, fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 64, None) == -1
-    assert f(fake(A), fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 32, None) == -2
+    assert f(fake(A), fake(A), fake(A), 0, 32, fake(A), 64, 256, 256, 64, None, 0, None) == 0
+    assert f(fake(A), fake(A), fake(A), 4, 24, fake(A), 64, 256, 256, 64, None, 0, None) == -4
+    assert f(fake(A), fake(A + 4), fake(A), 4, 32, fake(A), 64, 256, 256, 64, None, 0, None) == -3
+    assert f(None, fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 64, None, 0, None) == -1
+    assert f(fake(A), fake(A), fake(A), 4, 32, fake(A), 64, 256, 256, 32, None, 0, None) == -2
 
 
 def logprob(Lg=A, T=A, block=4096, out=A, t=4, V=248320, ldl=248320, ws=A, wsb=1 << 20):

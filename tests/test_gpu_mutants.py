@@ -1,14 +1,15 @@
 """GPU mutant tier: the GPU checks catch plausible mistakes in the library's reduction orders.
 
-tests/gpu_mutants.py builds five copies of the library, each with one mistake planted in one
+tests/gpu_mutants.py builds six copies of the library, each with one mistake planted in one
 translation unit (built beside the product by __graft_entry__.build()).  The same process loads each
 copy in turn in place of the product library and runs the order checks of tests/order_checks.py: the
 product must pass them all, and each mutant must fail at least the checks named for it below.  The
 checks are the ones the product's own GPU tests run (tests/test_gpu_schedule.py and the oracle
 comparisons of tests/test_gpu_logprob.py), so a mutant that passed here would pass those too.
 
-  k_plan_from_t               8 equal K slices when t > 16 (both projection kernels)
+  k_plan_from_t               8 equal K slices when t > 16 (the split and persistent kernels)
   slice_fold_reversed_from_t  the split kernel folds its slice sums from the last when t > 16
+  kslice_fold_reversed_from_t the small-N fold launch folds the slice sums from the last when t > 16
   block_fold_regrouped        the logprob fold adds four partials together before the running sum
   block_local_max             each block's exps are shifted by the block's own maximum
   in_block_tree_strided       the in-wave tree pairs lanes 32 apart first
@@ -29,8 +30,9 @@ from tests import gpu_mutants, order_checks  # noqa: E402
 from tests.gpu_util import say  # noqa: E402
 
 EXPECTED = {
-    "k_plan_from_t": {"split kernel", "persistent kernel"},
-    "slice_fold_reversed_from_t": {"split kernel"},
+    "k_plan_from_t": {"512 rows", "131172 rows"},
+    "slice_fold_reversed_from_t": {"512 rows"},
+    "kslice_fold_reversed_from_t": {"512 rows"},
     "block_fold_regrouped": {"fold order"},
     "block_local_max": {"random logits"},
     "in_block_tree_strided": {"in-block tree"},
@@ -40,6 +42,8 @@ EXPECTED = {
 @pytest.fixture(scope="module")
 def problems():
     say("mutant tier: building the order-sensitive problems")
+    # 512 rows: the K-slice kernels (with the queried workspace) and the split kernel (without);
+    # 131172 rows: the persistent kernel
     return (order_checks.OrderSensitiveProjection(21, 512, 5120, 32, 512),
             order_checks.OrderSensitiveProjection(22, 131172, 1024, 32, 2048))
 
@@ -47,8 +51,8 @@ def problems():
 def run_checks(problems) -> dict:
     split, persistent = problems
     return {
-        "split kernel": order_checks.check_projection(split),
-        "persistent kernel": order_checks.check_projection(persistent),
+        "512 rows": order_checks.check_projection(split),
+        "131172 rows": order_checks.check_projection(persistent),
         "random logits": order_checks.check_logprob_random(),
         "fold order": order_checks.check_logprob_fold_order(),
         "in-block tree": order_checks.check_logprob_in_block_tree(),
