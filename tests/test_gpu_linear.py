@@ -1,6 +1,6 @@
 """W8A16 fixed-width projection on the GPU, through the C ABI.
 
-Parity: every output within 2 bf16 ulps of the fp64 oracle (the north-star
+Parity: every output within 2 bf16 ulps of the fp64 oracle (the project's
 tolerance; the ninfer page, "Reading" paragraph under "Measured", puts
 schedule-to-schedule differences at 1-2 bf16 ulps).  Invariance: every column's
 bits are identical for every t <= T_pad, under column permutations, across
