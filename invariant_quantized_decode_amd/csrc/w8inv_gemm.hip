@@ -25,8 +25,9 @@
 //      keeping the running slice sum and the fold in registers, while the
 //      activation stage is shared through a double-buffered LDS ring.
 //  * Weight loads are coalesced.  Plain layout: one instruction covers 16 rows
-//    x 64 contiguous bytes (two groups) and v_permlane16_swap restores the
-//    matrix-core layout.  Packed layout (w8inv_pack.hip): one instruction
+//    x 64 contiguous bytes (two groups); the split kernel restores the
+//    matrix-core layout in registers with v_permlane16_swap, the persistent
+//    kernel reads it from an LDS slot that direct loads filled row by row.  Packed layout (w8inv_pack.hip): one instruction
 //    reads 1 KB of whole cache lines already in the matrix-core lane order,
 //    with the nontemporal cache policy (each byte is read once).
 //  * Each group's 32 products per output are summed by two chained
@@ -597,7 +598,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 //  * with SC (K/32 % 8 == 0 and 16-byte aligned scales) each lane loads its
 //    row's 8 scales of the next block with one 16-byte load; otherwise every
 //    stage loads its two scales per row (two 2-byte loads per lane);
-//  * weights run one block (BS stages) ahead in a register ring.
+//  * weights run one block (BS stages) ahead: in a register ring with the
+//    packed layout (its 1 KB loads are already in matrix-core lane order);
+//    with the plain layout in a per-wave LDS ring of 2 KB stage slots, filled
+//    by direct loads in which 4 consecutive lanes read one row's 64 bytes
+//    (whole 64-byte segments per lane quad: the register loads of 16 rows x
+//    64 bytes, one row per lane, took 4x the L1 accesses and ran 10% slower
+//    on a 248320 x 5120 head), the 16-byte slot of each piece XOR-swizzled by
+//    the row so that the matrix-core reads are free of bank conflicts.
 // The loads are issued in a fixed order, so every wait is a constant count.
 // ----------------------------------------------------------------------------
 constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
@@ -634,6 +642,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // MX: each wave's column maxima of its strip (value, NaN flag), per 32-column tile
     __shared__ float smax[MX ? kTileStrips * 32 * NT : 1];
     __shared__ int snan[MX ? kTileStrips * 32 * NT : 1];
+    // plain layout: each wave's weight stages, one 2 KB slot per stage of a block
+    __shared__ __align__(16) unsigned char wl[PK ? 16 : kTileStrips * kBlockStages * 2048];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -702,13 +712,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, blk * 128u + 4u * r, 0, kStreamOnce);
             return;
         }
+        {
+            // lane l: row 16 i + l / 4 of the strip, into slot l % 4 of that row's 64 bytes in
+            // the stage's LDS slot; the slot holds piece (l % 4) ^ (l / 16) (piece p: group
+            // p / 2 of the stage, 16-byte half p % 2)
+            const int k = lane >> 2;
+            const int piece = (lane & 3) ^ ((k >> 2) & 3);
+            const int gl = (piece >> 1) ? g1 : g;
+            unsigned char* slot = wl + (wave * kBlockStages + u) * 2048;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int64_t row = row0 + 16 * i + (lane & 15);
-            row = row < N ? row : N - 1;
-            const int gl = ((lane >> 4) & 1) ? g1 : g;
-            const uint32_t off = (uint32_t)(row * K) + (uint32_t)gl * kGroup + 16u * (lane >> 5);
-            st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+            for (int i = 0; i < 2; ++i) {
+                int64_t row = row0 + 16 * i + k;
+                row = row < N ? row : N - 1;
+                const uint32_t off = (uint32_t)(row * K) + (uint32_t)gl * kGroup + 16u * (uint32_t)(piece & 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, W8I_LDS(slot + 1024 * i), 16, off, 0, 0, 0);
+            }
         }
         if constexpr (!SC) {
             const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
@@ -773,9 +791,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // Only the values of the first XG column groups of 8 are computed (with
     // the packed layout the XL groups loaded, otherwise all): the others are
     // padding columns, never stored.
-    auto run = [&](auto XLc) {
+    auto run = [&](auto XLc, auto XGc) {
         constexpr int XL = decltype(XLc)::value;
-        constexpr int XG = PK ? XL : 4 * NT;
+        constexpr int XG = decltype(XGc)::value;
         if constexpr (XL < kXLoads) {
 #pragma unroll
             for (int i = XL; i < kXLoads; ++i) {
@@ -833,7 +851,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             };
             auto fetch = [&](int u, StageOps& o) {
                 WStage& cur = ring[u];
-                if constexpr (!PK) swap16(cur.w[0], cur.w[1]);
 #pragma unroll
                 for (int gs = 0; gs < 2; ++gs)
 #pragma unroll
@@ -846,8 +863,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                     }
 #pragma unroll
                 for (int gs = 0; gs < 2; ++gs) {
-                    o.lo[gs] = dequant8(cur.w[gs].x, cur.w[gs].y);
-                    o.hi[gs] = dequant8(cur.w[gs].z, cur.w[gs].w);
+                    u32x4 wv;
+                    if constexpr (PK) {
+                        wv = cur.w[gs];
+                    } else {
+                        // row r, piece 2 gs + c of the stage, from its swizzled slot: the 16
+                        // lanes of one LDS pass (rows 16 i .. 16 i + 15) hit 16 bank groups
+                        const int rr = r & 15, q = 2 * gs + c;
+                        wv = *reinterpret_cast<const u32x4*>(wl + (wave * kBlockStages + u) * 2048 + (r >> 4) * 1024 +
+                                                             rr * 64 + 16 * (q ^ ((rr >> 2) & 3)));
+                    }
+                    o.lo[gs] = dequant8(wv.x, wv.y);
+                    o.hi[gs] = dequant8(wv.z, wv.w);
                     uint16_t s16;
                     if constexpr (SC)
                         s16 = (uint16_t)(sc[u] >> (16 * gs));  // dword u: groups g0 + 2u, g0 + 2u + 1
@@ -981,15 +1008,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         // the phantom block's loads are still in flight: drain them before exit
         wait_vm<0>();
     };
+    using G1 = std::integral_constant<int, 1>;
+    using G2 = std::integral_constant<int, 2>;
+    using G3 = std::integral_constant<int, 3>;
+    using GAll = std::integral_constant<int, 4 * NT>;
     if constexpr (PK) {
         switch ((t + 7) / 8) {
-            case 1: run(std::integral_constant<int, 1>{}); break;
-            case 2: run(std::integral_constant<int, 2>{}); break;
-            case 3: run(std::integral_constant<int, kXLoads < 3 ? kXLoads : 3>{}); break;
-            default: run(std::integral_constant<int, kXLoads>{}); break;
+            case 1: run(G1{}, G1{}); break;
+            case 2: run(G2{}, G2{}); break;
+            case 3: run(std::integral_constant<int, kXLoads < 3 ? kXLoads : 3>{}, G3{}); break;
+            default: run(std::integral_constant<int, kXLoads>{}, GAll{}); break;
         }
     } else {
-        run(std::integral_constant<int, kXLoads>{});
+        using XAll = std::integral_constant<int, kXLoads>;
+        switch ((t + 7) / 8) {
+            case 1: run(XAll{}, G1{}); break;
+            case 2: run(XAll{}, G2{}); break;
+            case 3: run(XAll{}, G3{}); break;
+            default: run(XAll{}, GAll{}); break;
+        }
     }
 }
 
