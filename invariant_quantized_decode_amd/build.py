@@ -69,5 +69,43 @@ def build() -> str:
     return LIB
 
 
+# The host layer (argument validation, launch planning) with AddressSanitizer, for the CPU tests of
+# the C ABI: w8inv_api.hip built with ASan on its host side only (each -fsanitize= after -Xarch_host),
+# linked with the product's other objects; loaded with the ASan runtime preloaded.
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libw8inv_hostasan.so")
+HOST_ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime shared library of the ROCm toolchain ("" if absent)."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else ""
+
+
+def build_host_asan() -> str:
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    api = "w8inv_api.hip"
+    obj = os.path.join(ASAN_DIR, api.replace(".hip", ".o"))
+    r = subprocess.run([HIPCC, *FLAGS, *HOST_ASAN_FLAGS, "-c", os.path.join(CSRC, api), "-o", obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on the host-ASan build of " + api)
+    others = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES if s != api]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        others = [_compile(s) for s in SOURCES if s != api]
+    tmp = ASAN_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                        obj, *others, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc link failed (host-ASan library)")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     print(build())
