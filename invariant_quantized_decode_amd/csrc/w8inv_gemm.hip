@@ -692,26 +692,48 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         uint16_t s[2];
         uint32_t sp;  // packed: the row's two scales
     };
-    // weights (and per-stage scales) of stage u of block b
-    auto load_stage = [&](int b, int u, WStage& st) {
+    // Packed layout: where block b's stages start in this wave's strip, worked
+    // out once per block (stage u of the block is the strip's stage block
+    // block_g(b) / 2 + u, 2 KB of codes and 128 bytes of scales further on),
+    // and how many of its stages lie inside K (the others are phantoms).
+    // Strips past the last read the last one: valid memory, never stored.
+    struct BlockBase {
+        uint32_t w, s;  // byte offsets of stage 0's codes and scales
+        int nlive;      // stages of the block with g < G (0 past the last block)
+    };
+    auto block_base = [&](int b) -> BlockBase {
+        BlockBase bb{0u, 0u, 0};
+        if constexpr (PK) {
+            const int bc = b < nb ? b : nb - 1;
+            int64_t strip = (int64_t)tile_of(bc) * kTileStrips + wave;
+            strip = strip < strips ? strip : strips - 1;
+            const int p0 = block_g(bc) >> 1;
+            const uint32_t blk = (uint32_t)(strip * P + p0);
+            bb.w = blk * 2048u;
+            bb.s = blk * 128u;
+            bb.nlive = b < nb ? (nst - p0 < kBlockStages ? nst - p0 : kBlockStages) : 0;
+        }
+        return bb;
+    };
+    // weights (and per-stage scales) of stage u of block b (bb = block_base(b))
+    auto load_stage = [&](int b, int u, WStage& st, const BlockBase& bb) {
+        if constexpr (PK) {
+            // lane l takes bytes 16 l .. 16 l + 15 of each 1 KB half and its
+            // row's scale pair; the stage's offset is a scalar operand
+            const bool live = u < bb.nlive;
+            const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        wr, 1024u * i + 16u * lane, bb.w + 2048u * u, kStreamOnce));
+            st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, 4u * r, bb.s + 128u * u, kStreamOnce);
+            return;
+        }
         const int g = block_g(b) + 2 * u;
         const bool live = b < nb && g < G;
         const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
         const int g1 = g + 1 < G ? g + 1 : g;  // odd G: the last stage repeats its group
         const int64_t row0 = strip_row(b < nb ? b : nb - 1);
-        if constexpr (PK) {
-            // the strip's block of pair g / 2 (strips past the last read the
-            // last one: valid memory, never stored); lane l takes bytes
-            // 16 l .. 16 l + 15 of each 1 KB half and its row's scale pair
-            const int64_t strip = row0 / kRows < strips ? row0 / kRows : strips - 1;
-            const uint32_t blk = (uint32_t)(strip * P + g / 2);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        wr, blk * 2048u + 1024u * i + 16u * lane, 0, kStreamOnce));
-            st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, blk * 128u + 4u * r, 0, kStreamOnce);
-            return;
-        }
         {
             // lane l: row 16 i + l / 4 of the strip, into slot l % 4 of that row's 64 bytes in
             // the stage's LDS slot; the slot holds piece (l % 4) ^ (l / 16) (piece p: group
@@ -810,10 +832,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SC) sc0 = load_scales(0);
         __builtin_amdgcn_sched_barrier(0);
+        {
+            const BlockBase bb0 = block_base(0);
 #pragma unroll
-        for (int u = 0; u < kBlockStages; ++u) {
-            load_stage(0, u, ring[u]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int u = 0; u < kBlockStages; ++u) {
+                load_stage(0, u, ring[u], bb0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         // block b: activations in xs, scales in sc; block b + 1 is loaded into
@@ -834,6 +859,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             __builtin_amdgcn_sched_barrier(0);
             const bool live = b < nb;
             const int g0 = block_g(b);
+            const BlockBase nbb = block_base(b + 1);
             // A one-stage software pipeline.  fetch(u) reads stage u's matrix-core
             // A operands from LDS (the block's activations are all there since the
             // barrier), dequantises its weights from the register ring and decodes
@@ -916,7 +942,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                 // the loads keep their issue order (the waits count on it); other
                 // work may move across
                 __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
-                load_stage(b + 1, u, ring[u]);
+                load_stage(b + 1, u, ring[u], nbb);
                 __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
                 if (u + 1 < kBlockStages) {
                     // stage u + 1's loads: after them are pending the block's later
