@@ -224,21 +224,11 @@ __device__ __forceinline__ float exp32(float xf) {
 
 // ---------------------------------------------------------------- LOG32
 
-// LOG32(x) = RN32(ln x) for every fp32 x, in double-double:
-//   x = m 2^e with m in [sqrt(1/2), sqrt(2)); ln x = e ln2 + 2 atanh(z),
-//   z = (m - 1)/(m + 1), |z| <= 0.1716; atanh by its odd series to z^43.
-//   m - 1 and m + 1 are exact in double (m has 24 significant bits).
-__device__ __noinline__ float log32(float xf) {
-    if (xf != xf || xf < 0.0f) return __builtin_nanf("");
-    if (xf == 0.0f) return -__builtin_inff();
-    if (__builtin_isinf(xf)) return xf;
-    if (xf == 1.0f) return 0.0f;
-    int ex;
-    double m = __builtin_frexp((double)xf, &ex);  // m in [0.5, 1)
-    if (m < 0x1.6a09e667f3bcdp-1) {                // sqrt(1/2)
-        m *= 2.0;
-        ex -= 1;
-    }
+// ln(m 2^e) in double-double, m in [sqrt(1/2), sqrt(2)): ln x = e ln2 +
+// 2 atanh(z), z = (m - 1)/(m + 1), |z| <= 0.1716; atanh by its odd series to
+// z^43, Horner in double-double (error ~2^-100).  m - 1 and m + 1 are exact in
+// double (m has 24 significant bits).
+__device__ __noinline__ dd log_dd_reduced(double m, int ex) {
     const double num = m - 1.0, den = m + 1.0;
     const double q1 = num / den;
     const double rem = __builtin_fma(-q1, den, num);
@@ -256,9 +246,58 @@ __device__ __noinline__ float log32(float xf) {
     const double e = (double)ex;
     dd le = two_prod(e, kLn2Hi);
     le.lo += e * kLn2Lo1;
-    const dd s = dd_add(le, lnm);
-    if (s.hi < 0.0) return -rn32_dd_nonneg(-s.hi, -s.lo);
-    return rn32_dd_nonneg(s.hi, s.lo);
+    return dd_add(le, lnm);
+}
+
+// LOG32(x) = RN32(ln x) for every fp32 x.  x = m 2^e as above.
+//   Fast path, in double: the same atanh series to z^22 (the 12 terms of
+//   s = z^2 from s^0 / 1 to s^11 / 23; the next term is below 2^-65 of the
+//   sum), z = RN64((m - 1)/(m + 1)), lnm = 2 z P, v = fma(e, ln2_hi, lnm) +
+//   e ln2_lo.  Each of z, s, P (Horner: the last of its 11 fmas dominates,
+//   the earlier errors shrink by s <= 0.0295 per step) and z P rounds once:
+//   |lnm - ln m| <= 3.2 2^-53 |ln m|; for e != 0, |ln x| >= ln2 - ln sqrt 2 =
+//   0.3466 >= |ln m| and the fma and the final add round once each, so
+//   |v - ln x| <= 5.5 2^-53 |ln x| < 2^-50 |ln x| (and for e = 0, v = lnm).
+//   If v lies farther than 2^-47 |v| (8 times that bound) from the binary32
+//   rounding boundary on its side, RN32(v) = RN32(ln x); otherwise (about one
+//   input in 2^22) the double-double evaluation decides.
+__device__ __forceinline__ float log32(float xf) {
+    if (xf != xf || xf < 0.0f) return __builtin_nanf("");
+    if (xf == 0.0f) return -__builtin_inff();
+    if (__builtin_isinf(xf)) return xf;
+    if (xf == 1.0f) return 0.0f;
+    int ex;
+    double m = __builtin_frexp((double)xf, &ex);  // m in [0.5, 1)
+    if (m < 0x1.6a09e667f3bcdp-1) {                // sqrt(1/2)
+        m *= 2.0;
+        ex -= 1;
+    }
+    const double z = (m - 1.0) / (m + 1.0);
+    const double s = z * z;
+    double p = 1.0 / 23.0;
+    p = __builtin_fma(p, s, 1.0 / 21.0);
+    p = __builtin_fma(p, s, 1.0 / 19.0);
+    p = __builtin_fma(p, s, 1.0 / 17.0);
+    p = __builtin_fma(p, s, 1.0 / 15.0);
+    p = __builtin_fma(p, s, 1.0 / 13.0);
+    p = __builtin_fma(p, s, 1.0 / 11.0);
+    p = __builtin_fma(p, s, 1.0 / 9.0);
+    p = __builtin_fma(p, s, 1.0 / 7.0);
+    p = __builtin_fma(p, s, 1.0 / 5.0);
+    p = __builtin_fma(p, s, 1.0 / 3.0);
+    p = __builtin_fma(p, s, 1.0);
+    const double lnm = 2.0 * (z * p);
+    const double e = (double)ex;
+    const double v = __builtin_fma(e, kLn2Hi, lnm) + e * kLn2Lo1;
+    const float f = (float)v;  // RN32(-v) = -RN32(v): the check runs on |v|
+    const double a = __builtin_fabs(v);
+    const float fa = __builtin_fabsf(f);  // >= 2^-25: ln x != 0 for x != 1
+    const double d = a - (double)fa;
+    const double half = (d >= 0.0 ? f32_gap_up(fa) : f32_gap_down(fa)) * 0.5;
+    if (half - __builtin_fabs(d) > a * 0x1p-47) return f;
+    const dd sl = log_dd_reduced(m, ex);
+    if (sl.hi < 0.0) return -rn32_dd_nonneg(-sl.hi, -sl.lo);
+    return rn32_dd_nonneg(sl.hi, sl.lo);
 }
 
 }  // namespace w8i
