@@ -729,6 +729,33 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, 4u * r, bb.s + 128u * u, kStreamOnce);
             return;
         }
+        if constexpr (SC) {
+            // pairs of stages: after the second stage of pair u / 2 its slot takes
+            // the pair of block b, 4 loads of 8 rows x 128 bytes (whole lines: reading
+            // 64 bytes per row per load ran the same weights at 4.9 against 7.0 TB/s).
+            // Lane l of load i: row 8 i + l / 8 of the strip, into slot l % 8 of that
+            // row's 128 bytes in the pair's 4 KB LDS slot; slot s holds the row's piece
+            // s ^ (row / 2 % 8) (piece q: stage q / 4 of the pair, group q / 2 % 2,
+            // 16-byte half q % 2), so one LDS pass of 16 rows reads 16 bank groups.
+            // Past K (odd G, phantom stages) the loads bring bytes that are not used.
+            if ((u & 1) == 0) return;
+            const int pr = u >> 1;
+            const int gp = block_g(b) + 4 * pr;  // first group of the pair
+            const bool live = b < nb && gp < G;
+            const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
+            const int64_t row0 = strip_row(b < nb ? b : nb - 1);
+            unsigned char* slot = wl + (wave * (kBlockStages / 2) + pr) * 4096;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 8 * i + (lane >> 3);
+                int64_t row = row0 + rl;
+                row = row < N ? row : N - 1;
+                const uint32_t q = (uint32_t)((lane & 7) ^ ((rl >> 1) & 7));
+                const uint32_t off = (uint32_t)(row * K) + (uint32_t)gp * kGroup + 16u * q;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, W8I_LDS(slot + 1024 * i), 16, off, 0, 0, 0);
+            }
+            return;
+        }
         const int g = block_g(b) + 2 * u;
         const bool live = b < nb && g < G;
         const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
@@ -816,6 +843,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     auto run = [&](auto XLc, auto XGc) {
         constexpr int XL = decltype(XLc)::value;
         constexpr int XG = decltype(XGc)::value;
+        // a stage's weights have landed once only the loads issued after them are
+        // pending: the block's later stages, the next block's activations (and
+        // scales) and the next block's stages already reloaded -- the same count for
+        // every stage.  With pairs of stages (SC) that is the other pair's 4 loads:
+        // before the first pair's stages the block's second pair, before the second
+        // pair's the next block's first pair.
+        constexpr int kStageWait = SC ? 4 + XL + LS : (kBlockStages - 1) * LW + XL + LS;
         if constexpr (XL < kXLoads) {
 #pragma unroll
             for (int i = XL; i < kXLoads; ++i) {
@@ -892,6 +926,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                     u32x4 wv;
                     if constexpr (PK) {
                         wv = cur.w[gs];
+                    } else if constexpr (SC) {
+                        // row r, piece 4 (u % 2) + 2 gs + c of pair u / 2, from its swizzled slot
+                        const int q = 4 * (u & 1) + 2 * gs + c;
+                        wv = *reinterpret_cast<const u32x4*>(wl + (wave * (kBlockStages / 2) + (u >> 1)) * 4096 +
+                                                             r * 128 + 16 * (q ^ ((r >> 1) & 7)));
                     } else {
                         // row r, piece 2 gs + c of the stage, from its swizzled slot: the 16
                         // lanes of one LDS pass (rows 16 i .. 16 i + 15) hit 16 bank groups
@@ -915,7 +954,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             // stage 0's loads have landed once only the loads issued after them
             // are pending: the block's other stages, the next block's activations
             // (and scales)
-            wait_vm<(kBlockStages - 1) * LW + XL + LS>();
+            wait_vm<kStageWait>();
             fetch(0, ops[0]);
 #pragma unroll
             for (int u = 0; u < kBlockStages; ++u) {
@@ -948,7 +987,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                     // stage u + 1's loads: after them are pending the block's later
                     // stages, the next block's activations (and scales) and its
                     // stages 0..u -- the same count as for stage 0
-                    wait_vm<(kBlockStages - 1) * LW + XL + LS>();
+                    wait_vm<kStageWait>();
                     fetch(u + 1, ops[(u + 1) & 1]);
                 }
                 if (work) {
