@@ -5,6 +5,10 @@
  *   - w8c_stream_read: the practical HBM read ceiling of one launch -- a bare
  *     streaming read (16-byte nontemporal loads, 8 in flight per thread,
  *     512 threads per workgroup, each workgroup one contiguous chunk).
+ *   - w8c_strip_read: the read ceiling in the persistent projection's own
+ *     decomposition over the packed layout (tiles of 8 strips, one wave per
+ *     strip, 2 KB code blocks and 128-byte scale lines in order, 8 blocks in
+ *     flight per wave).
  *   - w8c_mfma_bf16: the dense bf16 matrix-core rate -- every wave issues
  *     independent v_mfma_f32_32x32x16_bf16 chains with no memory traffic.
  *
@@ -31,6 +35,15 @@ extern "C" {
  * W8I_ENULL, W8I_ESHAPE, W8I_EALIGN, W8I_EWORKSPACE (sink too small), W8I_EHIP. */
 int w8c_stream_read(const void *buf, int64_t bytes, int32_t workgroups, void *sink, size_t sink_bytes,
                     void *stream);
+
+/* Read `strips` x `pairs` blocks of 2048 bytes of `codes` (16-byte aligned) and 128 bytes of
+ * `scales` (4-byte aligned) -- the packed layout's codes and scales of a projection of 32
+ * strips rows and 64 pairs columns, strips * pairs * 2048 < 2^32 -- once, with `workgroups`
+ * (1..65536) workgroups of 8 waves: workgroup b takes tiles b, b + workgroups, ... of 8 strips,
+ * wave w strip w of its tile, each wave its strip's blocks in order.  `sink` as above.
+ * W8I_ENULL, W8I_ESHAPE, W8I_EALIGN, W8I_EWORKSPACE, W8I_EHIP. */
+int w8c_strip_read(const void *codes, const void *scales, int32_t strips, int32_t pairs, int32_t workgroups,
+                   void *sink, size_t sink_bytes, void *stream);
 
 /* Issue `workgroups` (1..65536) workgroups of 4 waves; each wave runs 4
  * independent chains of `iters` (1..2^20) v_mfma_f32_32x32x16_bf16, so one

@@ -29,6 +29,7 @@ def _lib():
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.w8c_stream_read.argtypes, L.w8c_stream_read.restype = [P, I64, I32, P, SZ, P], ctypes.c_int
         L.w8c_mfma_bf16.argtypes, L.w8c_mfma_bf16.restype = [I32, I32, P, SZ, P], ctypes.c_int
+        L.w8c_strip_read.argtypes, L.w8c_strip_read.restype = [P, P, I32, I32, I32, P, SZ, P], ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -71,6 +72,39 @@ def stream_read_gbs(nbytes: int, workgroups=(192, 256, 512, 1024, 2048), replays
         del graph
     del bufs, sink
     return out
+
+
+def strip_read_gbs(N: int, K: int, workgroups: int = 256, replays: int = 8) -> float:
+    """GB/s (codes + scales) of one launch that reads the packed layout of an [N, K] projection the
+    way the persistent projection streams it (w8c_strip_read), over copies totalling >= 1 GiB,
+    replayed from a HIP graph and timed with events on the graph's stream."""
+    import torch
+    L = _lib()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    strips, pairs = (N + 31) // 32, (K // 32 + 1) // 2
+    cb, sb = strips * pairs * 2048, strips * pairs * 128
+    copies = max(2, math.ceil((1 << 30) / (cb + sb)))
+    bufs = [(torch.zeros(cb, dtype=torch.uint8, device=dev), torch.zeros(sb, dtype=torch.uint8, device=dev))
+            for _ in range(copies)]
+    sink = torch.empty(workgroups * READ_THREADS, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for c, s in bufs:
+                _check(L.w8c_strip_read(c.data_ptr(), s.data_ptr(), strips, pairs, workgroups, sink.data_ptr(),
+                                        sink.numel() * 4, stream.cuda_stream), "w8c_strip_read")
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / (replays * copies)
+    del graph, bufs, sink
+    return (cb + sb) / sec / 1e9
 
 
 def mfma_bf16_tflops(workgroups: int = 4096, iters: int = 2048, launches: int = 3) -> float:

@@ -37,6 +37,47 @@ __global__ __launch_bounds__(kReadThreads) void stream_read(const u32x4* __restr
     if (x == kNever) sink[(int64_t)blockIdx.x * kReadThreads + threadIdx.x] = x;
 }
 
+// The persistent projection's decomposition over the packed layout: workgroup b takes tiles
+// b, b + gridDim.x, ... of 8 strips, wave w strip w of the tile; a strip is `pairs` blocks of
+// 2048 code bytes (two 1 KB loads) and 128 scale bytes (a 4-byte load per lane of the first 32),
+// read in order with kStripDepth blocks in flight per wave.  Every access goes through a buffer
+// descriptor of exactly strips * pairs * 2048 (codes) and strips * pairs * 128 (scales) bytes.
+constexpr int kStripDepth = 8;
+__global__ __launch_bounds__(kReadThreads) void strip_read(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales, int strips, int pairs,
+                                                          uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes), (short)0, (int)(uint32_t)((int64_t)strips * pairs * 2048), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales), (short)0, (int)(uint32_t)((int64_t)strips * pairs * 128), 0x00020000);
+    const int tiles = (strips + 7) / 8;
+    uint32_t x = 0;
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        int s = tile * 8 + wave;
+        s = s < strips ? s : strips - 1;
+        for (int p0 = 0; p0 < pairs; p0 += kStripDepth) {
+            u32x4 v[kStripDepth][2];
+            uint32_t sv[kStripDepth];
+#pragma unroll
+            for (int d = 0; d < kStripDepth; ++d) {
+                const int p = p0 + d < pairs ? p0 + d : pairs - 1;
+                const uint32_t blk = (uint32_t)s * (uint32_t)pairs + (uint32_t)p;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    v[d][i] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, 1024u * i + 16u * lane, blk * 2048u, 2));
+                sv[d] = __builtin_amdgcn_raw_buffer_load_b32(sr, 4u * (uint32_t)(lane & 31), blk * 128u, 2);
+            }
+#pragma unroll
+            for (int d = 0; d < kStripDepth; ++d)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) x ^= v[d][i].x ^ v[d][i].y ^ v[d][i].z ^ v[d][i].w ^ sv[d];
+        }
+    }
+    if (x == kNever) sink[(int64_t)blockIdx.x * kReadThreads + threadIdx.x] = x;
+}
+
 constexpr int kMfmaThreads = 256;  // 4 waves
 constexpr int kChains = 4;         // independent accumulators per wave
 
@@ -79,6 +120,22 @@ extern "C" int w8c_stream_read(const void* buf, int64_t bytes, int32_t workgroup
     hipLaunchKernelGGL(stream_read, dim3((unsigned)workgroups), dim3(kReadThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n16, per,
                        static_cast<uint32_t*>(sink));
+    return launch_status();
+}
+
+extern "C" int w8c_strip_read(const void* codes, const void* scales, int32_t strips, int32_t pairs,
+                              int32_t workgroups, void* sink, size_t sink_bytes, void* stream) {
+    if (codes == nullptr || scales == nullptr || sink == nullptr) return W8I_ENULL;
+    if (strips < 1 || pairs < 1 || (int64_t)strips * pairs * 2048 >= ((int64_t)1 << 32) || workgroups < 1 ||
+        workgroups > 65536)
+        return W8I_ESHAPE;
+    if ((reinterpret_cast<uintptr_t>(codes) & 15) != 0 || (reinterpret_cast<uintptr_t>(scales) & 3) != 0 ||
+        (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
+        return W8I_EALIGN;
+    if (sink_bytes < (size_t)workgroups * kReadThreads * sizeof(uint32_t)) return W8I_EWORKSPACE;
+    hipLaunchKernelGGL(strip_read, dim3((unsigned)workgroups), dim3(kReadThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(codes),
+                       static_cast<const uint8_t*>(scales), strips, pairs, static_cast<uint32_t*>(sink));
     return launch_status();
 }
 

@@ -291,7 +291,7 @@ def test_calibration_library_exports_its_header_and_validates():
     from invariant_quantized_decode_amd import calib
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "w8calib.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(w8c_[a-z0-9_]*)\s*\(", text)))
-    assert names == ["w8c_mfma_bf16", "w8c_stream_read"]
+    assert names == ["w8c_mfma_bf16", "w8c_stream_read", "w8c_strip_read"]
     C = calib._lib()
     for n in names:
         assert hasattr(C, n), n
@@ -305,6 +305,12 @@ def test_calibration_library_exports_its_header_and_validates():
     assert C.w8c_mfma_bf16(1, 0, fake, 1024, None) == -2
     assert C.w8c_mfma_bf16(0, 1, fake, 1024, None) == -2
     assert C.w8c_mfma_bf16(2, 1, fake, 1024, None) == -6
+    assert C.w8c_strip_read(fake, None, 8, 80, 1, fake, 2048, None) == -1
+    assert C.w8c_strip_read(fake, fake, 0, 80, 1, fake, 2048, None) == -2      # no strips
+    assert C.w8c_strip_read(fake, fake, 8, 1 << 20, 1, fake, 2048, None) == -2  # 2^32 bytes of codes or more
+    assert C.w8c_strip_read(fake, fake, 8, 80, 0, fake, 2048, None) == -2      # no workgroups
+    assert C.w8c_strip_read(ctypes.c_void_p(264), fake, 8, 80, 1, fake, 2048, None) == -3
+    assert C.w8c_strip_read(fake, fake, 8, 80, 2, fake, 2048, None) == -6      # sink for one workgroup only
 
 
 def test_kernel_digest_follows_code_not_comments():

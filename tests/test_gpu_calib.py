@@ -22,6 +22,12 @@ def test_stream_read_rate_is_plausible():
         assert math.isfinite(gbs) and 500.0 < gbs < 8000.0, (wg, gbs)
 
 
+def test_strip_read_rate_is_plausible():
+    gbs = calib.strip_read_gbs(6144, 5120, workgroups=256, replays=2)
+    say(f"strip read GB/s: {gbs:.1f}")
+    assert math.isfinite(gbs) and 500.0 < gbs < 8000.0
+
+
 def test_mfma_rate_is_plausible():
     tf = calib.mfma_bf16_tflops(workgroups=1024, iters=512, launches=2)
     say(f"mfma bf16 TFLOP/s: {tf:.1f}")
