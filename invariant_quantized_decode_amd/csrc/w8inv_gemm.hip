@@ -600,12 +600,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 //    stage loads its two scales per row (two 2-byte loads per lane);
 //  * weights run one block (BS stages) ahead: in a register ring with the
 //    packed layout (its 1 KB loads are already in matrix-core lane order);
-//    with the plain layout in a per-wave LDS ring of 2 KB stage slots, filled
-//    by direct loads in which 4 consecutive lanes read one row's 64 bytes
-//    (whole 64-byte segments per lane quad: the register loads of 16 rows x
-//    64 bytes, one row per lane, took 4x the L1 accesses and ran 10% slower
-//    on a 248320 x 5120 head), the 16-byte slot of each piece XOR-swizzled by
-//    the row so that the matrix-core reads are free of bank conflicts.
+//    with the plain layout in a per-wave LDS ring filled by direct loads, the
+//    16-byte slot of each piece XOR-swizzled by the row so that the
+//    matrix-core reads are free of bank conflicts: with SC, 4 KB slots of two
+//    stages, each refilled after its second stage by loads of 8 rows x 128
+//    bytes (whole lines: a bare read of the head with 64 bytes per row per
+//    load ran at 4.9 TB/s, with 128 at 7.0); otherwise 2 KB stage slots, 4
+//    lanes per row's 64 bytes (register loads of 16 rows x 64 bytes, one row
+//    per lane, took 4x the L1 accesses and ran 10% slower).
 // The loads are issued in a fixed order, so every wait is a constant count.
 // ----------------------------------------------------------------------------
 constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
