@@ -333,10 +333,10 @@ int vocab_block_logprob_direct(const uint16_t *logits, const int64_t *targets, i
  * formed from logits shifted by it); the projection as for
  * w8_linear_invariant.  The fixed arithmetic needs the row's global maximum
  * before any block partial, so only that first pass can join the head
- * projection: its workgroups write, with the logits, the column maxima of
- * each 256-row tile they store (exact in any order), and the logprob's
- * block-partial and fold kernels take the row maximum from those per-tile
- * maxima instead of a pass over the logits.
+ * projection: each of its workgroups writes, with the logits, the column
+ * maxima over all the rows it stores (exact in any order), and the logprob's
+ * block-partial and fold kernels take the row maximum from those
+ * per-workgroup maxima instead of a pass over the logits.
  *
  *   logits = w8_linear_invariant(W_q, scales, x, t, T_pad)        bit for bit
  *   out    = vocab_block_logprob(logits, targets, block)          bit for bit
@@ -348,7 +348,8 @@ int vocab_block_logprob_direct(const uint16_t *logits, const int64_t *targets, i
  * kernel (the one w8_linear_invariant runs for N >= 131072 at T_pad <= 32):
  * T_pad 16 or 32, or 48 / 64 with t <= 32 (W8I_ET otherwise).  workspace:
  * 16-byte aligned, at least w8_head_logprob_workspace_bytes(t, V, block)
- * bytes (per-tile maxima [t, ceil(V/256)] and block partials [t, ceil(V/block)]
+ * bytes (room for per-workgroup maxima [t, ceil(V/256)] -- one workgroup per
+ * CU, at most one per 256-row tile -- and block partials [t, ceil(V/block)]
  * in fp32); contents are scratch.  The _packed form takes w8_pack's layout.
  * ------------------------------------------------------------------------- */
 size_t w8_head_logprob_workspace_bytes(int32_t t, int64_t V, int32_t block);

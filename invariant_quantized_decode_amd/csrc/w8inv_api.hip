@@ -308,10 +308,11 @@ static int head_logprob(bool packed, const int8_t* W, const uint16_t* S, const u
     if (st != W8I_OK) return st;
     if (!workspace || workspace_bytes < w8_head_logprob_workspace_bytes(t, V, block)) return W8I_EWORKSPACE;
     if (!aligned(workspace, 16)) return W8I_EALIGN;
-    st = launch_linear_max(packed, W, S, x, t, T_pad, logits, V, K, ldx, ldl, static_cast<float*>(workspace),
+    int nm = 0;  // column maxima per row the projection writes (one per workgroup), at most tiles_of(V)
+    st = launch_linear_max(packed, W, S, x, t, T_pad, logits, V, K, ldx, ldl, static_cast<float*>(workspace), &nm,
                            as_stream(stream));
     if (st != W8I_OK) return st;
-    return launch_logprob_from_max(logits, targets, block, out, t, V, ldl, workspace, tiles_of(V), as_stream(stream));
+    return launch_logprob_from_max(logits, targets, block, out, t, V, ldl, workspace, nm, as_stream(stream));
 }
 
 int w8_head_logprob_invariant(const int8_t* W_q, const uint16_t* scales, const uint16_t* x, const int64_t* targets,

@@ -612,15 +612,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 // ----------------------------------------------------------------------------
 constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
 
+// DPP controls (GFX9 encoding) for the max epilogue's cross-lane reduction
+constexpr int kDppIdentity = 0xE4;       // quad_perm [0, 1, 2, 3]
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i of each 8 takes lane 7 - i
+constexpr int kDppRowMirror = 0x140;      // lane i of each 16 takes lane 15 - i
+constexpr int kDppRowBcast15 = 0x142;     // lane 15 of each row to every lane of the next row
+
+// Order key of a stored bf16 value for the max epilogue: the fp32 bit pattern
+// with the magnitude bits of negative values flipped, so that a signed-integer
+// comparison orders numbers as floats do (-0 below +0: either zero may be the
+// maximum of a tie); NaN takes the largest key, so any NaN wins, and rows past
+// the last (valid false) the key of -inf.
+constexpr int kKeyNaN = 0x7FFFFFFF;
+constexpr int kKeyNegInf = (int)0x807FFFFFu;
+__device__ __forceinline__ int mx_key(uint16_t b, bool valid) {
+    const int bits = (int)((uint32_t)b << 16);
+    const int k = (b & 0x7FFF) > 0x7F80 ? kKeyNaN : bits ^ ((bits >> 31) & 0x7FFFFFFF);
+    return valid ? k : kKeyNegInf;
+}
+// the float a key stands for (the canonical NaN for the NaN key)
+__device__ __forceinline__ float mx_value(int k) {
+    return k == kKeyNaN ? __builtin_nanf("") : __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+
 // PK: packed layout (w8_pack): each stage's weights are the strip's 2 KB block
 // and its scales one 128-byte line, loaded with the stage.
 // MX: the logprob's max epilogue (the head projection fused with the first
-// step of the blockwise logprob): besides storing the tile's outputs, the
-// workgroup writes, for every live column j, the maximum over the tile's rows
-// n < N of the stored values (bf16 widened exactly to fp32), or NaN if one of
-// them is NaN, to M[j * ldm + tile].  A maximum is exact in any order, so the
-// row maximum the logprob takes from these per-tile maxima is the one it would
-// take from the logits.
+// step of the blockwise logprob): besides storing the outputs, the workgroup
+// writes, for every live column j, the maximum over the rows n < N of all its
+// tiles of the stored values (bf16 widened exactly to fp32), or NaN if one of
+// them is NaN, to M[j * ldm + workgroup].  A maximum is exact in any order, so
+// the row maximum the logprob takes from these per-workgroup maxima is the one
+// it would take from the logits.
 template <int TP16, bool SC, bool PK, bool MX = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     const int8_t* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ X,
@@ -641,9 +666,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // one array per buffer, so each buffer's direct loads are told apart
     __shared__ __align__(16) unsigned char xb0[kBlockBytes];
     __shared__ __align__(16) unsigned char xb1[kBlockBytes];
-    // MX: each wave's column maxima of its strip (value, NaN flag), per 32-column tile
-    __shared__ float smax[MX ? kTileStrips * 32 * NT : 1];
-    __shared__ int snan[MX ? kTileStrips * 32 * NT : 1];
+    // MX: the workgroup's running column maxima (order keys), per 32-column tile
+    __shared__ int skey[MX ? 32 * NT : 1];
     // plain layout: each wave's weight stages, one 2 KB slot per stage of a block
     __shared__ __align__(16) unsigned char wl[PK ? 16 : kTileStrips * kBlockStages * 2048];
 
@@ -655,6 +679,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     const int my_tiles = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int nb = my_tiles * nbt;                                // blocks of this workgroup
     const int r = lane & 31, c = lane >> 5;
+    if constexpr (MX) {
+        if (wave == 0 && lane < 32)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) skey[tt * 32 + lane] = kKeyNegInf;
+        __syncthreads();
+    }
 
     // packed layout: whole strips of P = ceil(G/2) stage blocks (2 KB of codes, 128 bytes of scales)
     const int64_t P = (G + 1) / 2;
@@ -1011,57 +1041,62 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
                 // the tile's last block: fold the remaining slices, store this strip
                 while (slice < kKSlices) fold_slice();
                 const int64_t n = strip_row(b) + r;
+                uint16_t bv[NT][16];
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) bv[tt][v] = f64_to_bf16(total[tt][v]);
                 if (n < N) {
+                    // the lane's column half through an identity DPP move here: a convergent
+                    // operation, which the compiler keeps inside this branch, so the store
+                    // addresses are formed at the stores instead of being held in registers
+                    // across the loop
+                    const int ce = __builtin_amdgcn_mov_dpp(c, kDppIdentity, 0xF, 0xF, false);
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                         for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
-                            const int j = 32 * tt + 8 * (v >> 2) + 4 * c + (v & 3);
-                            if (j < t) Y[(int64_t)j * ldy + n] = f64_to_bf16(total[tt][v]);
+                            const int j = 32 * tt + 8 * (v >> 2) + 4 * ce + (v & 3);
+                            if (j < t) Y[(int64_t)j * ldy + n] = bv[tt][v];
                         }
                 }
                 if constexpr (MX) {
-                    // lane (r, c) holds row r of the strip for columns 8 (v / 4) + 4 c + v % 4:
-                    // reduce over the 32 lanes of each half (xor 1 .. 16 keeps c), so that
-                    // lanes 0 and 32 hold the strip's column maxima; the 8 strips meet in LDS
+                    // lane (r, c) holds row r of the strip for columns 8 (v / 4) + 4 c + v % 4.
+                    // Each stored value becomes an order key (mx_key: a signed-integer max
+                    // of keys is the float max; NaN has the largest key, rows past N the key
+                    // of -inf), and the keys are reduced over the 32 lanes of each half with
+                    // DPP moves: within each row of 16 lanes (quad swaps, half-row and row
+                    // mirrors), then row 0 into row 1 and row 2 into row 3 (row_bcast:15),
+                    // so lanes 16 and 48 hold the strip's column maxima, which join the
+                    // workgroup's running maxima in LDS (atomic max)
+                    int key[NT][16];
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                        for (int v = 0; v < ((tt == NT - 1) ? kLastValues : 16); ++v) {
-                            const float val = bf16_to_f32(f64_to_bf16(total[tt][v]));
-                            float m = n < N && val == val ? val : -__builtin_inff();
-                            int nan = n < N && val != val ? 1 : 0;
+                        for (int v = 0; v < tile_live_values(tt, XG, (tt == NT - 1) ? kLastValues : 16); ++v)
+                            key[tt][v] = mx_key(bv[tt][v], n < N);
+                    // one DPP step over every key at a time (independent moves back to back);
+                    // the last step writes rows 1 and 3 only, the others are not read
+                    auto reduce_step = [&](auto ctrl, auto row_mask) {
 #pragma unroll
-                            for (int off = 1; off < 32; off <<= 1) {
-                                m = __builtin_fmaxf(m, __shfl_xor(m, off));
-                                nan |= __shfl_xor(nan, off);
-                            }
-                            const int j = 8 * (v >> 2) + 4 * c + (v & 3);
-                            if (r == 0) {
-                                smax[(wave * NT + tt) * 32 + j] = m;
-                                snan[(wave * NT + tt) * 32 + j] = nan;
-                            }
-                        }
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                    __builtin_amdgcn_s_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                    if (wave == 0) {
-                        // lane l: column l of each tile
+                        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                        for (int tt = 0; tt < NT; ++tt) {
-                            const int j = 32 * tt + (lane & 31);
-                            float m = -__builtin_inff();
-                            int nan = 0;
+                            for (int v = 0; v < tile_live_values(tt, XG, (tt == NT - 1) ? kLastValues : 16); ++v)
+                                key[tt][v] = max(key[tt][v], __builtin_amdgcn_mov_dpp(key[tt][v], decltype(ctrl)::value,
+                                                                                      decltype(row_mask)::value, 0xF, true));
+                    };
+                    using RowsAll = std::integral_constant<int, 0xF>;
+                    reduce_step(std::integral_constant<int, kDppQuadSwap1>{}, RowsAll{});
+                    reduce_step(std::integral_constant<int, kDppQuadSwap2>{}, RowsAll{});
+                    reduce_step(std::integral_constant<int, kDppRowHalfMirror>{}, RowsAll{});
+                    reduce_step(std::integral_constant<int, kDppRowMirror>{}, RowsAll{});
+                    reduce_step(std::integral_constant<int, kDppRowBcast15>{}, std::integral_constant<int, 0xA>{});
+                    if (r == 16) {
 #pragma unroll
-                            for (int w = 0; w < kTileStrips; ++w) {
-                                m = __builtin_fmaxf(m, smax[(w * NT + tt) * 32 + (lane & 31)]);
-                                nan |= snan[(w * NT + tt) * 32 + (lane & 31)];
-                            }
-                            if (lane < 32 && j < t) M[(int64_t)j * ldm + b / nbt * (int)gridDim.x + (int)blockIdx.x] =
-                                                         nan ? __builtin_nanf("") : m;
-                        }
+                        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                            for (int v = 0; v < tile_live_values(tt, XG, (tt == NT - 1) ? kLastValues : 16); ++v)
+                                atomicMax(&skey[tt * 32 + 8 * (v >> 2) + 4 * c + (v & 3)], key[tt][v]);
                     }
                 }
                 slice = 0;
@@ -1074,6 +1109,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         }
         // the phantom block's loads are still in flight: drain them before exit
         wait_vm<0>();
+        if constexpr (MX) {
+            // every wave's last tile has met the running maxima: wave 0 writes them
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (wave == 0 && lane < 32)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    if (32 * tt + lane < t)
+                        M[(int64_t)(32 * tt + lane) * ldm + (int)blockIdx.x] = mx_value(skey[tt * 32 + lane]);
+        }
     };
     using G1 = std::integral_constant<int, 1>;
     using G2 = std::integral_constant<int, 2>;
@@ -1102,20 +1150,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
 static int tile_count(int64_t N) { return (int)((N + kTileStrips * kRows - 1) / (kTileStrips * kRows)); }
 
 // scales: 0 per-stage 2-byte loads, 1 eight scales per 16-byte load (SC), 2 packed layout (PK)
-// M != nullptr: the max epilogue (MX), per-tile column maxima into M [t][ldm = tile count]
+// M != nullptr: the max epilogue (MX), per-workgroup column maxima into M [t][ldm = workgroups],
+// the number of workgroups into *nm
 static int launch_tiles(const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad, uint16_t* Y,
                         int64_t N, int64_t K, int64_t ldx, int64_t ldy, int scales, hipStream_t stream,
-                        float* M = nullptr) {
+                        float* M = nullptr, int* nm = nullptr) {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return W8I_EHIP;
     const int ntiles = tile_count(N);
     const dim3 grid((unsigned)(ntiles < ncu ? ntiles : ncu)), block(kGemmThreads);
+    if (nm) *nm = (int)grid.x;
 #define W8I_TILES_LAUNCH(TP, SCV, PKV)                                                                            \
     if (M)                                                                                                        \
         hipLaunchKernelGGL((gemm_w8g32_tiles<TP, SCV, PKV, true>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, \
-                           ldy, ntiles, M, (int64_t)ntiles);                                                      \
+                           ldy, ntiles, M, (int64_t)grid.x);                                                      \
     else                                                                                                          \
         hipLaunchKernelGGL((gemm_w8g32_tiles<TP, SCV, PKV>), grid, block, 0, stream, W, S, X, Y, N, K, t, ldx, ldy, \
                            ntiles, nullptr, (int64_t)0)
@@ -1330,15 +1380,16 @@ int launch_linear_packed(const int8_t* Wp, const uint16_t* Sp, const uint16_t* X
 int tiles_of(int64_t N) { return tile_count(N); }
 
 // the head projection on the persistent kernel with the max epilogue: y as w8_linear_invariant
-// (or _packed) gives it, and M [t][tiles_of(N)] the per-tile column maxima; T_pad <= 32 (or 48 / 64
-// with t <= 32)
+// (or _packed) gives it, and M [t][*nm] the column maxima of each of its *nm <= tiles_of(N)
+// workgroups; T_pad <= 32 (or 48 / 64 with t <= 32)
 int launch_linear_max(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
-                      uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, float* M, hipStream_t stream) {
+                      uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, float* M, int* nm,
+                      hipStream_t stream) {
     T_pad = kernel_width(t, T_pad);
     if (T_pad > 32) return W8I_ET;
     const bool s16 = (reinterpret_cast<uintptr_t>(S) & 15) == 0;
     const int scales = packed ? 2 : ((K / kGroup) % 8 == 0 && s16 ? 1 : 0);
-    return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, scales, stream, M);
+    return launch_tiles(W, S, X, t, T_pad, Y, N, K, ldx, ldy, scales, stream, M, nm);
 }
 
 int launch_linear_pair(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,

@@ -88,10 +88,12 @@ int launch_logprob(const uint16_t* L, const int64_t* targets, int block, float* 
 size_t logprob_from_max_workspace_bytes(int t, int64_t V, int block, int nm);
 int launch_logprob_from_max(const uint16_t* L, const int64_t* targets, int block, float* out, int t, int64_t V,
                             int64_t ldl, void* ws, int nm, hipStream_t stream);
-// the persistent projection with the max epilogue (per-tile column maxima into M [t][tiles_of(N)])
+// the persistent projection with the max epilogue: per-workgroup column maxima into M [t][*nm],
+// *nm (the number of workgroups) at most tiles_of(N)
 int tiles_of(int64_t N);
 int launch_linear_max(bool packed, const int8_t* W, const uint16_t* S, const uint16_t* X, int t, int T_pad,
-                      uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, float* M, hipStream_t stream);
+                      uint16_t* Y, int64_t N, int64_t K, int64_t ldx, int64_t ldy, float* M, int* nm,
+                      hipStream_t stream);
 // device address of the current device's fixed scratch array (W8I_NOALLOC_SCRATCH_BYTES bytes),
 // looked up once per device; allocates nothing
 int noalloc_scratch(void** ptr);

@@ -142,7 +142,7 @@ __device__ __forceinline__ float row_max_from_blocks(const float* M, int nb, int
 }
 
 // M holds nm partial maxima per column (the nb block maxima, or the head
-// projection's per-tile maxima when it ran with the max epilogue).
+// projection's per-workgroup maxima when it ran with the max epilogue).
 template <int E, bool VEC>
 __global__ __launch_bounds__(kLpThreads) void lp_block_sumexp(const uint16_t* __restrict__ L, int64_t V,
                                                               int64_t ldl, int nb, const float* __restrict__ M,

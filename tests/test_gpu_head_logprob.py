@@ -2,7 +2,7 @@
 
 tokenspeed numerics ("Logprobs", block_sumexp leaf contract) fixes the logprob's arithmetic: the row
 maximum first, then block partials of exps shifted by it, folded left to right.  The fused call moves
-only the first pass into the head projection (per-tile column maxima written with the logits; a maximum
+only the first pass into the head projection (per-workgroup column maxima written with the logits; a maximum
 is exact in any order), so both of its results must equal the unfused calls bit for bit:
 
   logits == w8_linear_invariant(W, S, x)           out == vocab_block_logprob(logits, targets, block)
