@@ -612,6 +612,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_split_lds(
 // ----------------------------------------------------------------------------
 constexpr int kTileStrips = kKSlices;  // 8 waves, one 32-row strip each
 
+// a raw buffer descriptor of p with the given range in bytes (0: every load returns zeros
+// with no memory access)
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const T* p, int range) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), (short)0, range, 0x00020000);
+}
+
 // DPP controls (GFX9 encoding) for the max epilogue's cross-lane reduction
 constexpr int kDppIdentity = 0xE4;       // quad_perm [0, 1, 2, 3]
 constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]
@@ -689,15 +696,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
     // packed layout: whole strips of P = ceil(G/2) stage blocks (2 KB of codes, 128 bytes of scales)
     const int64_t P = (G + 1) / 2;
     const int64_t strips = (N + kRows - 1) / kRows;
-    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(W), (short)0, (int)(uint32_t)(PK ? strips * P * 2048 : N * K), 0x00020000);
-    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S), (short)0, (int)(uint32_t)(PK ? strips * P * 128 : N * G * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(X), (short)0, (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(W), (short)0, 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t s_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(S), (short)0, 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t x_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, 0, 0x00020000);
+    // the buffers' ranges in bytes: a load goes through a descriptor with its buffer's
+    // range, or with range 0 (phantom stages, blocks past the last), which returns zeros
+    // with no memory access; only the range word differs, so one scalar select picks it
+    const int w_range = (int)(uint32_t)(PK ? strips * P * 2048 : N * K);
+    const int s_range = (int)(uint32_t)(PK ? strips * P * 128 : N * G * 2);
+    const int x_range = (int)(uint32_t)(((int64_t)(t - 1) * ldx + K) * 2);
 
     // direct load i of this wave covers load m = kXLoads * wave + i of the
     // block: stage m / (4 NT), tile (m / 4) % NT, columns 8 (m % 4) .. + 7
@@ -753,12 +757,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             // lane l takes bytes 16 l .. 16 l + 15 of each 1 KB half and its
             // row's scale pair; the stage's offset is a scalar operand
             const bool live = u < bb.nlive;
-            const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
+            const __amdgpu_buffer_rsrc_t wr = range_rsrc(W, live ? w_range : 0);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 st.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         wr, 1024u * i + 16u * lane, bb.w + 2048u * u, kStreamOnce));
-            st.sp = __builtin_amdgcn_raw_buffer_load_b32(live ? s_rsrc : s_none, 4u * r, bb.s + 128u * u, kStreamOnce);
+            st.sp = __builtin_amdgcn_raw_buffer_load_b32(range_rsrc(S, live ? s_range : 0), 4u * r, bb.s + 128u * u, kStreamOnce);
             return;
         }
         if constexpr (SC) {
@@ -774,7 +778,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             const int pr = u >> 1;
             const int gp = block_g(b) + 4 * pr;  // first group of the pair
             const bool live = b < nb && gp < G;
-            const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
+            const __amdgpu_buffer_rsrc_t wr = range_rsrc(W, live ? w_range : 0);
             const int64_t row0 = strip_row(b < nb ? b : nb - 1);
             unsigned char* slot = wl + (wave * (kBlockStages / 2) + pr) * 4096;
 #pragma unroll
@@ -790,7 +794,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         }
         const int g = block_g(b) + 2 * u;
         const bool live = b < nb && g < G;
-        const __amdgpu_buffer_rsrc_t wr = live ? w_rsrc : w_none;
+        const __amdgpu_buffer_rsrc_t wr = range_rsrc(W, live ? w_range : 0);
         const int g1 = g + 1 < G ? g + 1 : g;  // odd G: the last stage repeats its group
         const int64_t row0 = strip_row(b < nb ? b : nb - 1);
         {
@@ -810,7 +814,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             }
         }
         if constexpr (!SC) {
-            const __amdgpu_buffer_rsrc_t sr = live ? s_rsrc : s_none;
+            const __amdgpu_buffer_rsrc_t sr = range_rsrc(S, live ? s_range : 0);
             int64_t row = row0 + r;
             row = row < N ? row : N - 1;
             const uint32_t off = (uint32_t)(row * G) * 2u;
@@ -824,7 +828,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         int64_t row = strip_row(live ? b : nb - 1) + r;
         row = row < N ? row : N - 1;
         const uint32_t off = (uint32_t)(row * G + block_g(b < nb ? b : nb - 1)) * 2u;
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? s_rsrc : s_none, off, 0, 0));
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(range_rsrc(S, live ? s_range : 0), off, 0, 0));
     };
     // this wave's share of block b's activations, into buffer xb (its first
     // XL = XLc direct loads)
@@ -834,7 +838,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         const uint32_t g_off = (uint32_t)block_g(live ? b : nb - 1) * 64u;
 #pragma unroll
         for (int i = 0; i < XL; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? x_rsrc : x_none, W8I_LDS(xb + xl_off[i]), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(range_rsrc(X, live ? x_range : 0), W8I_LDS(xb + xl_off[i]), 16,
                                                      xg_off[i] + g_off, 0, 0, 0);
     };
 
