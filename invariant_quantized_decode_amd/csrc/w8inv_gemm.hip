@@ -718,6 +718,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
         xl_off[i] = (uint32_t)(st * kStageBytes + tt * kXTileBytes + (8 * (m % 4)) * 128);
     }
 
+    // plain layout with 8-scale loads: this lane's offset within pair load i (row
+    // 8 i + l / 8 of the strip, its swizzled 16-byte piece, see load_stage); the
+    // strip's and the pair's offsets are added per load
+    uint32_t wl_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rl = 8 * i + (lane >> 3);
+        wl_off[i] = (uint32_t)(rl * K) + 16u * (uint32_t)((lane & 7) ^ ((rl >> 1) & 7));
+    }
+
     // tile of block b, first group of block b (wave-uniform)
     auto tile_of = [&](int b) { return (int)blockIdx.x + (b / nbt) * (int)gridDim.x; };
     auto strip_row = [&](int b) { return (int64_t)tile_of(b) * (kTileStrips * kRows) + (int64_t)wave * kRows; };
@@ -779,17 +789,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_w8g32_tiles(
             const int gp = block_g(b) + 4 * pr;  // first group of the pair
             const bool live = b < nb && gp < G;
             const __amdgpu_buffer_rsrc_t wr = range_rsrc(W, live ? w_range : 0);
-            const int64_t row0 = strip_row(b < nb ? b : nb - 1);
+            // rows past N (the last strip of a ragged N) lie past the range: their
+            // loads bring zeros without a memory access, and they are never stored
+            const uint32_t base = (uint32_t)(strip_row(b < nb ? b : nb - 1) * K) + (uint32_t)gp * kGroup;
             unsigned char* slot = wl + (wave * (kBlockStages / 2) + pr) * 4096;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rl = 8 * i + (lane >> 3);
-                int64_t row = row0 + rl;
-                row = row < N ? row : N - 1;
-                const uint32_t q = (uint32_t)((lane & 7) ^ ((rl >> 1) & 7));
-                const uint32_t off = (uint32_t)(row * K) + (uint32_t)gp * kGroup + 16u * q;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, W8I_LDS(slot + 1024 * i), 16, off, 0, 0, 0);
-            }
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, W8I_LDS(slot + 1024 * i), 16, wl_off[i] + base, 0, 0, 0);
             return;
         }
         const int g = block_g(b) + 2 * u;
