@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY.  Each mutant plants one plausible mistake in a copy of one translation unit
 of the library -- a reduction schedule chosen from t, a reordered fold (of the slice sums, in one launch
 or in the small-N fold launch, or of the logprob's block partials), a local instead of a global shift, a
-different in-block tree -- and is linked with the product's other objects into
+different in-block tree, a row maximum taken over rows past the vocabulary -- and is linked with the product's other objects into
 tests/mutant_libs/lib_<name>.so.  The GPU tests load each one beside the product library and check
 that their invariance and parity checks catch it while the product passes them.  Every mutation keeps
 all memory accesses and loop bounds of the code it replaces (no mutant can fault or hang).  The
@@ -62,6 +62,10 @@ MUTANTS = {
         ("    const float m = row_max_from_blocks<kLpThreads>(M, nm, j, nan);\n    if (nan) {",
          "    float m = row_max_from_blocks<kLpThreads>(M, nm, j, nan);\n    m = nm == nb ? M[(int64_t)j * nm + b] : m;\n"
          "    if (nan) {"),
+    ]),
+    # the fused head's max epilogue counts every row of the last strip, the rows past V too
+    "max_epilogue_counts_padding_rows": ("w8inv_gemm.hip", [
+        ("key[tt][v] = mx_key(bv[tt][v], n < N);", "key[tt][v] = mx_key(bv[tt][v], true);"),
     ]),
     # the in-wave butterfly of a block's tree pairs lanes 32 apart first (strided halves)
     "in_block_tree_strided": ("w8inv_logprob.hip", [

@@ -5,7 +5,7 @@ fp64 sum by about 1e-16 relative, which decides a bf16 rounding for no output in
 projection checks therefore run on synth.order_sensitive_linear, where most outputs change with the
 order, and compare with tests/order_model.py's model of the documented schedule and across t.  The
 logprob checks use random logits and two constructed rows on which one fp32 rounding tells two orders
-apart.
+apart; the fused-maxima check, a ragged vocabulary of negative logits.
 
 Each check returns a list of failure descriptions (empty: passed).  They call the binding's current
 library, so the mutant tier runs them unchanged on each mutated build.  Test infrastructure only.
@@ -127,3 +127,29 @@ def check_logprob_fold_order() -> list:
 def check_logprob_in_block_tree() -> list:
     logits, targets, block = strided_tree_row()
     return _compare_logprob("in-block tree row", logits, targets, block)
+
+
+def check_fused_maxima() -> list:
+    """The fused head's row maxima on a vocabulary that is not a multiple of the 32-row strip, every
+    logit below -104 (positive codes and scales, negative activations): the last strip's rows past V
+    compute zeros, and a maximum that counted them would be 0, under which every exp underflows
+    (a maximum of 0 over logits near -60 can still give the same bits).  Both layouts' fused calls
+    must give the unfused calls' logprob bits."""
+    rng = np.random.default_rng(31)
+    V, K, t, block = 4013, 256, 5, 256
+    q = rng.integers(1, 128, size=(V, K), dtype=np.int8)
+    s = synth.draw_scales(rng, V, K, 0.08)
+    x = synth.draw_acts(rng, t, K) | np.uint16(0x8000)
+    targets = rng.integers(0, V, size=t, dtype=np.int64)
+    Wd, Sd, Xd, Td = i8(q), f16(s), bf16(x), torch.from_numpy(targets).to(DEV)
+    logits = w8.w8_linear_invariant(Wd, Sd, Xd, t, 32)
+    want = host(w8.vocab_block_logprob(logits, Td, block)).view(np.uint32)
+    assert float(logits.float().max()) < -104.0, "every logit below -104"
+    Wp, Sp = w8.w8_pack(Wd, Sd)
+    fails = []
+    for name, out in (("plain", w8.w8_head_logprob_invariant(Wd, Sd, Xd, Td, t, 32, block)[1]),
+                      ("packed", w8.w8_head_logprob_invariant_packed(Wp, Sp, Xd, Td, t, 32, block, V)[1])):
+        bad = int(np.count_nonzero(host(out).view(np.uint32) != want))
+        if bad:
+            fails.append(f"fused maxima ({name}): {bad} of {t} logprobs differ from the unfused calls'")
+    return fails

@@ -99,3 +99,26 @@ def test_fused_head_refuses_two_tiles_and_small_workspace():
         w8.w8_head_logprob_invariant(Wd, Sd, Xd[:4], Td, 4, 32, 4096,
                                      workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
     assert math.isfinite(float(host(w8.w8_head_logprob_invariant(Wd, Sd, Xd[:4], Td, 4, 64, 4096)[1])[0]))
+
+
+@pytest.mark.parametrize("V,K", [(131149, 1024), (70001, 2048)])
+def test_fused_head_maxima_skip_rows_past_the_vocabulary(V, K):
+    """Every logit below -104 (positive codes and scales, negative activations), V not a multiple of
+    the 32-row strip: the rows past V that the last strip computes (zeros) must not enter the fused
+    row maxima -- if they did, the row maximum would be 0, every exp would underflow and every
+    logprob would differ from the unfused call's."""
+    rng = np.random.default_rng(V + 7)
+    q = rng.integers(1, 128, size=(V, K), dtype=np.int8)
+    s = synth.draw_scales(rng, V, K, 0.08)
+    x = synth.draw_acts(rng, 32, K)
+    x = x | np.uint16(0x8000)                       # every activation negative (or -0)
+    targets = rng.integers(0, V, size=32, dtype=np.int64)
+    Wd, Sd, Xd, Td = i8(q), f16(s), bf16(x), torch.from_numpy(targets).to(DEV)
+    Pk = w8.w8_pack(Wd, Sd)
+    for t in (1, 32):
+        say(f"case fused head negative logits V={V} K={K} t={t}")
+        ref_l, ref_o, plain, packed = run_both(Wd, Sd, Pk, Xd, Td, t, 32, 4096, V)
+        assert np.all((ref_l & 0x8000) != 0) and np.all((ref_l & 0x7FFF) > 0x42D0), "every logit below -104"
+        for name, (lg, o) in (("plain", plain), ("packed", packed)):
+            assert np.array_equal(lg, ref_l), f"{name} t={t}: logits differ"
+            assert np.array_equal(f32bits(o), f32bits(ref_o)), f"{name} t={t}: logprob differs"

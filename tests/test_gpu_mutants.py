@@ -1,6 +1,6 @@
 """GPU mutant tier: the GPU checks catch plausible mistakes in the library's reduction orders.
 
-tests/gpu_mutants.py builds six copies of the library, each with one mistake planted in one
+tests/gpu_mutants.py builds seven copies of the library, each with one mistake planted in one
 translation unit (built beside the product by __graft_entry__.build()).  The same process loads each
 copy in turn in place of the product library and runs the order checks of tests/order_checks.py: the
 product must pass them all, and each mutant must fail at least the checks named for it below.  The
@@ -13,6 +13,7 @@ comparisons of tests/test_gpu_logprob.py), so a mutant that passed here would pa
   block_fold_regrouped        the logprob fold adds four partials together before the running sum
   block_local_max             each block's exps are shifted by the block's own maximum
   in_block_tree_strided       the in-wave tree pairs lanes 32 apart first
+  max_epilogue_counts_padding_rows  the fused head's row maxima count the last strip's rows past V
 
 Every mutation keeps the memory accesses and loop bounds of the code it replaces.
 """
@@ -36,6 +37,7 @@ EXPECTED = {
     "block_fold_regrouped": {"fold order"},
     "block_local_max": {"random logits"},
     "in_block_tree_strided": {"in-block tree"},
+    "max_epilogue_counts_padding_rows": {"fused maxima"},
 }
 
 
@@ -56,6 +58,7 @@ def run_checks(problems) -> dict:
         "random logits": order_checks.check_logprob_random(),
         "fold order": order_checks.check_logprob_fold_order(),
         "in-block tree": order_checks.check_logprob_in_block_tree(),
+        "fused maxima": order_checks.check_fused_maxima(),
     }
 
 
